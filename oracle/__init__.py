@@ -1,0 +1,320 @@
+"""CPU oracle for the compressed-moment Adam step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``adam_oracle.c`` (plain,
+scalar fp32 C; see that file's header for the sources and the pins) with
+ctypes; this module only marshals numpy arrays, it does no arithmetic of the
+method.  It imports nothing from the HIP implementation and shares no code
+with it.
+
+Storage modes are named by strings here: "f32" (oracle-only textbook mode
+with fp32 moments), "bf16", "q8" (int8 m + uint8 v, one fp32 scale per
+block each) and "q8_v_only" (fp32 m + uint8 v).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_STORAGE = {"f32": 0, "bf16": 1, "q8": 2, "q8_v_only": 3}
+_lib = None
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """Load (building first if absent) the oracle's shared library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIBRARY):
+        _build.build()
+    L = ctypes.CDLL(_build.LIBRARY)
+    L.orc_bf16_from_f32_array.argtypes = [_f32p, _u16p, ctypes.c_int64]
+    L.orc_f32_from_bf16_array.argtypes = [_u16p, _f32p, ctypes.c_int64]
+    L.orc_philox4x32_10.argtypes = [_u32p, _u32p, _u32p]
+    L.orc_sr_draws.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64,
+                               ctypes.c_int64, ctypes.c_int32, _u16p]
+    L.orc_percentile_rank.argtypes = [ctypes.c_float, ctypes.c_int64]
+    L.orc_percentile_rank.restype = ctypes.c_int64
+    L.orc_block_stat.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float]
+    L.orc_block_stat.restype = ctypes.c_float
+    L.orc_dequantize_block.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_float, _f32p]
+    L.orc_quantize_with_stat.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_float, _u16p, _i32p]
+    L.orc_quantize_with_stat.restype = ctypes.c_float
+    L.orc_quantize_block.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_float, _u16p, _i32p]
+    L.orc_quantize_block.restype = ctypes.c_float
+    L.orc_host_scalars.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                   ctypes.c_float, ctypes.c_int64, ctypes.c_int32, _f32p]
+    L.orc_adam_step.argtypes = (
+        [ctypes.c_int32, _i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
+        + [_vp] * 8
+        + [ctypes.c_float] * 6
+        + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64]
+        + [_vp, _vp])
+    L.orc_adam_step.restype = ctypes.c_int
+    L.orc_adam_step_blocks.argtypes = (
+        [ctypes.c_int64, _i64p, _i64p, _i64p, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
+        + [_vp] * 8
+        + [ctypes.c_float] * 6
+        + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64])
+    L.orc_adam_step_blocks.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _ptr(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+def _vptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+# --------------------------------------------------------------------------
+# element-level helpers
+# --------------------------------------------------------------------------
+def bf16_from_f32(x):
+    x = _c(x, np.float32).ravel()
+    out = np.empty(x.size, np.uint16)
+    lib().orc_bf16_from_f32_array(_ptr(x, _f32p), _ptr(out, _u16p), x.size)
+    return out
+
+
+def f32_from_bf16(h):
+    h = _c(h, np.uint16).ravel()
+    out = np.empty(h.size, np.float32)
+    lib().orc_f32_from_bf16_array(_ptr(h, _u16p), _ptr(out, _f32p), h.size)
+    return out
+
+
+def philox4x32_10(ctr, key):
+    c = _c(ctr, np.uint32)
+    k = _c(key, np.uint32)
+    assert c.size == 4 and k.size == 2
+    out = np.empty(4, np.uint32)
+    lib().orc_philox4x32_10(_ptr(c, _u32p), _ptr(k, _u32p), _ptr(out, _u32p))
+    return out
+
+
+def sr_draws(seed, t, gidx0, n, which):
+    """16-bit stochastic-rounding draws; which=0 first moment, 1 second."""
+    out = np.empty(n, np.uint16)
+    lib().orc_sr_draws(seed, t, gidx0, n, which, _ptr(out, _u16p))
+    return out
+
+
+def percentile_rank(p, n):
+    return int(lib().orc_percentile_rank(p, n))
+
+
+def block_stat(a, use_pct=False, p=99.9):
+    a = _c(a, np.float32).ravel()
+    return float(lib().orc_block_stat(_ptr(a, _f32p), a.size, int(use_pct), p))
+
+
+def dequantize_block(codes, signed, A):
+    c = _c(codes, np.int32).ravel()
+    out = np.empty(c.size, np.float32)
+    lib().orc_dequantize_block(_ptr(c, _i32p), c.size, int(signed), A, _ptr(out, _f32p))
+    return out
+
+
+def quantize_with_stat(x, signed, A, draws=None):
+    x = _c(x, np.float32).ravel()
+    codes = np.empty(x.size, np.int32)
+    d = None if draws is None else _c(draws, np.uint16).ravel()
+    A_out = lib().orc_quantize_with_stat(_ptr(x, _f32p), x.size, int(signed), A,
+                                         None if d is None else _ptr(d, _u16p),
+                                         _ptr(codes, _i32p))
+    return codes, np.float32(A_out)
+
+
+def quantize_block(x, signed, use_pct=False, p=99.9, draws=None):
+    x = _c(x, np.float32).ravel()
+    codes = np.empty(x.size, np.int32)
+    d = None if draws is None else _c(draws, np.uint16).ravel()
+    A = lib().orc_quantize_block(_ptr(x, _f32p), x.size, int(signed), int(use_pct), p,
+                                 None if d is None else _ptr(d, _u16p),
+                                 _ptr(codes, _i32p))
+    return codes, np.float32(A)
+
+
+def host_scalars(lr, beta1, beta2, wd, t, decoupled=True):
+    """(step, ibc2, decay, 1-beta1, 1-beta2) as fp32."""
+    out = np.empty(5, np.float32)
+    lib().orc_host_scalars(lr, beta1, beta2, wd, t, int(decoupled), _ptr(out, _f32p))
+    return out
+
+
+# --------------------------------------------------------------------------
+# multi-tensor state + step
+# --------------------------------------------------------------------------
+def pad16(n):
+    return (n + 15) // 16 * 16
+
+
+class OracleState:
+    """Flat, padded optimizer state held in numpy arrays (all zero at start).
+
+    numels: element counts of the tensors, in order; block: block length.
+    Buffers present per storage mode:
+      f32:        m_f32, v_f32
+      bf16:       m_bf16, v_bf16 (uint16 bit patterns)
+      q8:         m_codes (int8), v_codes (uint8), m_scale, v_scale
+      q8_v_only:  m_f32, v_codes, v_scale
+    """
+
+    def __init__(self, numels, storage, block=2048, grad_bf16=False):
+        self.numels = [int(n) for n in numels]
+        self.storage = storage
+        self.block = int(block)
+        self.grad_bf16 = bool(grad_bf16)
+        self.total = sum(pad16(n) for n in self.numels)
+        self.nblocks = sum((n + self.block - 1) // self.block for n in self.numels)
+        T, B = self.total, self.nblocks
+        self.m_f32 = self.v_f32 = self.m_bf16 = self.v_bf16 = None
+        self.m_codes = self.v_codes = self.m_scale = self.v_scale = None
+        if storage == "f32":
+            self.m_f32 = np.zeros(T, np.float32)
+            self.v_f32 = np.zeros(T, np.float32)
+        elif storage == "bf16":
+            self.m_bf16 = np.zeros(T, np.uint16)
+            self.v_bf16 = np.zeros(T, np.uint16)
+        elif storage == "q8":
+            self.m_codes = np.zeros(T, np.int8)
+            self.v_codes = np.zeros(T, np.uint8)
+            self.m_scale = np.zeros(B, np.float32)
+            self.v_scale = np.zeros(B, np.float32)
+        elif storage == "q8_v_only":
+            self.m_f32 = np.zeros(T, np.float32)
+            self.v_codes = np.zeros(T, np.uint8)
+            self.v_scale = np.zeros(B, np.float32)
+        else:
+            raise ValueError(storage)
+
+    def buffers(self):
+        names = ["m_codes", "v_codes", "m_scale", "v_scale", "m_bf16", "v_bf16",
+                 "m_f32", "v_f32"]
+        return {k: getattr(self, k) for k in names if getattr(self, k) is not None}
+
+    def step(self, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
+             decoupled=True, stochastic=False, percentile=None, seed=42,
+             want_moments=False):
+        """Advance params (list of float32 arrays, updated in place).
+
+        grads: float32 arrays, or uint16 bf16 bit patterns if grad_bf16.
+        percentile=None selects the absmax statistic.
+        Returns (m_new, v_new) flat padded fp32 arrays if want_moments.
+        """
+        n = len(self.numels)
+        assert len(params) == n and len(grads) == n
+        gdt = np.uint16 if self.grad_bf16 else np.float32
+        for k in range(n):
+            assert params[k].dtype == np.float32 and params[k].flags.c_contiguous
+            assert params[k].size == self.numels[k]
+            assert grads[k].dtype == gdt and grads[k].size == self.numels[k]
+        numels = np.array(self.numels, np.int64)
+        P = (ctypes.c_void_p * max(n, 1))(*[p.ctypes.data for p in params])
+        G = (ctypes.c_void_p * max(n, 1))(*[np.ascontiguousarray(g).ctypes.data
+                                             for g in grads])
+        m_new = v_new = None
+        if want_moments:
+            m_new = np.zeros(self.total, np.float32)
+            v_new = np.zeros(self.total, np.float32)
+        use_pct = percentile is not None
+        rc = lib().orc_adam_step(
+            n, _ptr(numels, _i64p), self.block, _STORAGE[self.storage], int(self.grad_bf16),
+            ctypes.cast(P, _vp), ctypes.cast(G, _vp),
+            _vptr(self.m_codes), _vptr(self.v_codes), _vptr(self.m_scale), _vptr(self.v_scale),
+            _vptr(self.m_bf16), _vptr(self.v_bf16), _vptr(self.m_f32), _vptr(self.v_f32),
+            lr, beta1, beta2, eps, weight_decay, percentile if use_pct else 100.0,
+            t, int(decoupled), int(stochastic), int(use_pct), seed,
+            _vptr(m_new), _vptr(v_new))
+        if rc != 0:
+            raise ValueError("oracle rejected the step arguments")
+        if want_moments:
+            return m_new, v_new
+        return None
+
+
+class OracleBlocks:
+    """State for a sample of independent blocks (full-size workloads).
+
+    blocks: list of (n, gidx) -- element count and first padded flat index of
+    each sampled block.  State for block i lives at offset off[i] of flat
+    arrays sized to the sample; scale slot i.
+    """
+
+    def __init__(self, blocks, storage, grad_bf16=False):
+        self.n = np.array([b[0] for b in blocks], np.int64)
+        self.gidx = np.array([b[1] for b in blocks], np.int64)
+        self.off = np.zeros(len(blocks), np.int64)
+        if len(blocks):
+            self.off[1:] = np.cumsum([pad16(int(x)) for x in self.n])[:-1]
+        total = int(sum(pad16(int(x)) for x in self.n))
+        self.inner = OracleState([], storage, grad_bf16=grad_bf16)
+        self.storage = storage
+        self.grad_bf16 = bool(grad_bf16)
+        B = len(blocks)
+        s = self.inner
+        if storage == "bf16":
+            s.m_bf16 = np.zeros(total, np.uint16)
+            s.v_bf16 = np.zeros(total, np.uint16)
+        elif storage == "q8":
+            s.m_codes = np.zeros(total, np.int8)
+            s.v_codes = np.zeros(total, np.uint8)
+            s.m_scale = np.zeros(B, np.float32)
+            s.v_scale = np.zeros(B, np.float32)
+        elif storage == "q8_v_only":
+            s.m_f32 = np.zeros(total, np.float32)
+            s.v_codes = np.zeros(total, np.uint8)
+            s.v_scale = np.zeros(B, np.float32)
+        elif storage == "f32":
+            s.m_f32 = np.zeros(total, np.float32)
+            s.v_f32 = np.zeros(total, np.float32)
+
+    def buffers(self):
+        return self.inner.buffers()
+
+    def block_slice(self, i):
+        o = int(self.off[i])
+        return slice(o, o + int(self.n[i]))
+
+    def step(self, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
+             decoupled=True, stochastic=False, percentile=None, seed=42):
+        """params[i]/grads[i]: arrays of block i (params updated in place)."""
+        B = len(self.n)
+        gdt = np.uint16 if self.grad_bf16 else np.float32
+        for i in range(B):
+            assert params[i].dtype == np.float32 and params[i].size == self.n[i]
+            assert grads[i].dtype == gdt and grads[i].size == self.n[i]
+        P = (ctypes.c_void_p * max(B, 1))(*[p.ctypes.data for p in params])
+        G = (ctypes.c_void_p * max(B, 1))(*[g.ctypes.data for g in grads])
+        s = self.inner
+        use_pct = percentile is not None
+        rc = lib().orc_adam_step_blocks(
+            B, _ptr(self.n, _i64p), _ptr(self.gidx, _i64p), _ptr(self.off, _i64p),
+            _STORAGE[self.storage], int(self.grad_bf16),
+            ctypes.cast(P, _vp), ctypes.cast(G, _vp),
+            _vptr(s.m_codes), _vptr(s.v_codes), _vptr(s.m_scale), _vptr(s.v_scale),
+            _vptr(s.m_bf16), _vptr(s.v_bf16), _vptr(s.m_f32), _vptr(s.v_f32),
+            lr, beta1, beta2, eps, weight_decay, percentile if use_pct else 100.0,
+            t, int(decoupled), int(stochastic), int(use_pct), seed)
+        if rc != 0:
+            raise ValueError("oracle rejected the step arguments")
