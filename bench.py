@@ -1,0 +1,197 @@
+"""Benchmark: one compressed-moment Adam step over a full parameter set.
+
+A step is one adam_step call through the C ABI -- one kernel launch over
+every tensor of the set (dequantize / bias-corrected update / block
+statistic / requantize, or the bf16-moment variant) -- on synthetic inputs
+already resident in HBM.  Default workload: the ViT-Base shaped set (152
+tensors, 86,567,656 fp32 params, fp32 grads ~N(0, 1e-3)) with bf16 moments.
+Other sets: --config (see workloads.CONFIGS).
+
+Prints one JSON line: Gparams/s, the roofline of the step kernel
+(algorithmic bytes per launch / average launch time from HIP events on the
+launch stream, against the 8 TB/s HBM peak; HBM traffic from rocprofv3
+FETCH_SIZE / WRITE_SIZE counters when a committed counter summary matches
+the current kernel source) and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "memory_efficient_adam_amd", "csrc", "adam_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+# algorithmic bytes per parameter (read + write) and per block (scales)
+#   params 4+4, grads 4 (fp32) or 2 (bf16), moments read+write, scales 4+4 per
+#   block per quantized moment
+_MOMENT_BYTES = {"bf16": 8, "q8": 4, "q8_v_only": 10}
+_SCALE_BYTES = {"bf16": 0, "q8": 16, "q8_v_only": 8}
+
+
+def algorithmic_bytes(cfg):
+    numels = cfg.numels()
+    n = sum(numels)
+    blocks = sum(-(-k // 2048) for k in numels)
+    g = 2 if cfg.grad_dtype == "bf16" else 4
+    return n * (8 + g + _MOMENT_BYTES[cfg.storage]) + blocks * _SCALE_BYTES[cfg.storage]
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload)
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(cfg, steps=1):
+    """The oracle, as it is, on one full step of the same workload (single
+    thread), same recipe of inputs generated on the host."""
+    import numpy as np  # noqa: F401
+    import oracle
+    import workloads
+    numels = cfg.numels()
+    params = workloads.host_params(cfg.cfg_id, numels)
+    st = oracle.OracleState(numels, cfg.storage, grad_bf16=(cfg.grad_dtype == "bf16"))
+    elapsed = 0.0
+    for t in range(1, steps + 1):
+        grads = workloads.host_grads(cfg.cfg_id, numels, t, dist=cfg.grad_dist,
+                                     dtype=cfg.grad_dtype)
+        t0 = time.perf_counter()
+        st.step(params, grads, t=t, **cfg.hp)
+        elapsed += time.perf_counter() - t0
+    n = sum(numels)
+    return {"value": round(n * steps / elapsed / 1e9, 5), "unit": "Gparams/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} full step(s) of the {cfg.name} workload ({n} params), "
+                      "single-threaded, host-generated inputs; generation not timed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="vit_bf16")
+    ap.add_argument("--grad-buffers", type=int, default=4,
+                    help="distinct pre-generated gradient sets used in rotation")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time torch's device copy of 4 GiB (counter calibration run)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the step needs no "
+              "exchange between GPUs); run with --gpus 1", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import memory_efficient_adam_amd as ma
+    import workloads
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 30  # 4 GiB of fp32 each way
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}), flush=True)
+        return
+
+    cfg = workloads.CONFIGS[args.config]
+    numels = cfg.numels()
+    n_params = sum(numels)
+    params = workloads.device_params(cfg.cfg_id, numels)
+    gsets = []
+    for i in range(max(1, args.grad_buffers)):
+        gsets.append(workloads.device_grads(cfg.cfg_id, numels, i + 1, dist=cfg.grad_dist,
+                                            dtype=cfg.grad_dtype))
+    st = ma.adam_state_create(numels, cfg.storage, cfg.grad_dtype)
+    stream = torch.cuda.current_stream()
+    hp = dict(cfg.hp)
+
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        ma.adam_step(st, params, gsets[t % len(gsets)], t=t, stream=stream, **hp)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        t += 1
+        ma.adam_step(st, params, gsets[t % len(gsets)], t=t, stream=stream, **hp)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = start.elapsed_time(end) / args.steps
+    sec = ms / 1e3
+
+    alg = algorithmic_bytes(cfg)
+    achieved = alg / sec / 1e9
+    traffic = traffic_for(cfg.name)
+    out = {
+        "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",
+        "value": round(n_params / sec / 1e9, 3),
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "params": n_params,
+            "tensors": len(numels),
+            "blocks": sum(-(-k // 2048) for k in numels),
+            "storage": cfg.storage,
+            "grad_dtype": cfg.grad_dtype,
+            "stochastic_rounding": bool(hp.get("stochastic")),
+            "percentile": hp.get("percentile"),
+            "block_size": 2048,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg,
+        },
+    }
+    st.destroy()
+    del params, gsets
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * adam_mi355x.h -- C ABI of the compressed-moment Adam/AdamW step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the Adam parameter update whose optimizer state is kept
+ * compressed, as two pages describe it:
+ *   - "feat: add 8-bit Adam optimizer for memory efficiency" (AiDotNet PR
+ *     #814): block-wise 8-bit state, one scale per block (default block
+ *     2048), signed first moment / unsigned second moment, scales recomputed
+ *     every step ("dynamic"), optional fp32 first moment
+ *     (CompressBothMoments=false), optional stochastic rounding, optional
+ *     percentile-based scale (default 99.9); each step dequantizes, applies
+ *     the bias-corrected Adam update and requantizes (walkthrough sequence
+ *     diagram); memory accounting (GetMemoryUsage); option validation
+ *     (BlockSize > 0, percentile within 0..100: review comments).
+ *   - "perf(training): make BF16-Adam fused-compatible (proper bf16 moment
+ *     kernel, not a gate)" (AiDotNet PR #1745): first and second moments in
+ *     half-size bf16 buffers updated by one fused Adam/AdamW kernel; the
+ *     optimizer configuration that a compiled step was set up with is checked
+ *     on every step so that a changed moment-storage flag is not missed
+ *     (review comment on the drift-detection tuple).
+ *
+ * Numerics of one element (fp32, each operation rounded once; g widened
+ * exactly from bf16 when grads are bf16):
+ *   [Adam, L2-coupled:  g = fma(wd, p, g)]
+ *   m = fma(beta1, m_old, (1-beta1)*g)
+ *   v = fma(beta2, v_old, (1-beta2)*(g*g))
+ *   p = fma(-lr/(1-beta1^t), m / fma(sqrt(v), 1/sqrt(1-beta2^t), eps), p*decay)
+ * with decay = 1 - lr*wd for AdamW and 1 for Adam, the bias-correction
+ * scalars formed in fp64 on the host and rounded once to fp32.  bf16
+ * storage rounds to nearest, ties to even.  8-bit storage: per block the
+ * statistic A (max |x|, or the percentile entry of |x| -- falling back to
+ * the max when that entry is below 2^-112) is stored as the fp32 scale; a
+ * code q decodes to (q * fl(1/qmax)) * A with qmax = 127 (m, int8, -128
+ * never produced) or 255 (v, uint8); encoding rounds |x| * fl(qmax/A) to
+ * nearest-even (or stochastically: up iff u < frac with u a 16-bit draw of
+ * Philox4x32-10, key = seed, counter = (flat index / 4, t), word = flat
+ * index mod 4, low half for m and high half for v) and pins |x| >= A to
+ * qmax; a block with A < 2^-112 stores zero codes and scale 0.
+ *
+ * State layout (device memory owned by the library): tensor k's segment has
+ * pad16(numel_k) entries and starts at the sum of the earlier segments (its
+ * "flat index" range); blocks of 2048 elements are numbered tensor-major,
+ * one fp32 scale per block per quantized moment.  Padding entries stay 0.
+ *
+ * Threading: calls on one state must be ordered (same stream, or the caller
+ * synchronizes); different states are independent.  All device work is
+ * enqueued on the caller's HIP stream (hipStream_t passed as void*; NULL is
+ * the null stream); argument errors are reported synchronously before any
+ * device work.  adam_last_error() returns a thread-local message for the
+ * last failing call on the calling thread.
+ */
+#ifndef ADAM_MI355X_H
+#define ADAM_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct adam_state adam_state; /* opaque; owns all optimizer-state memory */
+
+enum adam_status {
+    ADAM_OK = 0,
+    ADAM_EINVAL = -1,  /* bad argument or hyperparameter (see each call) */
+    ADAM_EMODE = -2,   /* layout passed to adam_step differs from the one at create */
+    ADAM_EALIGN = -3,  /* a param/grad pointer is not 16-byte aligned */
+    ADAM_ENOMEM = -4,  /* device or pinned-host allocation failed */
+    ADAM_EDEVICE = -5  /* a HIP call failed (includes launch errors) */
+};
+
+enum adam_storage {
+    ADAM_STORE_BF16 = 1,     /* m, v: bf16 (round to nearest even) */
+    ADAM_STORE_Q8 = 2,       /* m: int8 [-127,127], v: uint8, fp32 scale per block each */
+    ADAM_STORE_Q8_V_ONLY = 3 /* m: fp32, v: uint8 + fp32 scale per block */
+};
+
+enum adam_grad_dtype { ADAM_GRAD_F32 = 0, ADAM_GRAD_BF16 = 1 };
+
+enum adam_flags {
+    ADAM_F_DECOUPLED_WD = 1u, /* AdamW (p *= 1 - lr*wd); else Adam with L2 (g += wd*p) */
+    ADAM_F_STOCHASTIC = 2u,   /* 8-bit storage only: Philox stochastic rounding; else nearest-even */
+    ADAM_F_PERCENTILE = 4u    /* 8-bit storage only: percentile block statistic; else absmax */
+};
+
+enum adam_buffer {
+    ADAM_BUF_M_CODES = 0, /* int8[padded elements]     (Q8) */
+    ADAM_BUF_V_CODES = 1, /* uint8[padded elements]    (Q8, Q8_V_ONLY) */
+    ADAM_BUF_M_SCALE = 2, /* float[blocks]             (Q8) */
+    ADAM_BUF_V_SCALE = 3, /* float[blocks]             (Q8, Q8_V_ONLY) */
+    ADAM_BUF_M_BF16 = 4,  /* uint16[padded elements]   (BF16) */
+    ADAM_BUF_V_BF16 = 5,  /* uint16[padded elements]   (BF16) */
+    ADAM_BUF_M_F32 = 6    /* float[padded elements]    (Q8_V_ONLY) */
+};
+
+#define ADAM_BLOCK_SIZE 2048 /* the only block size the gfx950 kernels take */
+
+typedef struct {
+    int32_t storage;    /* enum adam_storage */
+    int32_t grad_dtype; /* enum adam_grad_dtype */
+    int32_t block_size; /* must be ADAM_BLOCK_SIZE */
+} adam_layout;
+
+typedef struct {
+    float lr;           /* >= 0, finite */
+    float beta1;        /* in [0, 1) */
+    float beta2;        /* in [0, 1) */
+    float eps;          /* > 0, finite */
+    float weight_decay; /* >= 0, finite */
+    float percentile;   /* in [0, 100]; read only with ADAM_F_PERCENTILE */
+    int64_t t;          /* 1-based step number (bias correction, SR counter) */
+    uint32_t flags;     /* enum adam_flags */
+    uint32_t reserved;  /* must be 0 */
+    uint64_t seed;      /* Philox key for stochastic rounding */
+} adam_hparams;
+
+/*
+ * Bytes of optimizer state for a tensor list, without allocating:
+ *   sum_k pad16(numel_k) * e + blocks * s, with (e, s) = (4, 0) for BF16,
+ *   (2, 8) for Q8 and (5, 4) for Q8_V_ONLY.
+ * The per-block descriptor table (16 bytes per block) and the per-tensor
+ * pointer table (16 bytes per tensor) are bookkeeping, not counted.
+ * Memory accounting follows the 8-bit Adam page (GetMemoryUsage).
+ * Pure host function.  Returns < 0 (an adam_status) on bad arguments:
+ * n_tensors < 0, numels NULL with n_tensors > 0, numel < 0 or >= 2^32,
+ * layout NULL or invalid.
+ */
+int64_t adam_state_bytes(int32_t n_tensors, const int64_t *numels, const adam_layout *layout);
+
+/*
+ * Creates a state for n_tensors tensors of the given element counts (zero
+ * counts allowed; n_tensors may be 0) on the current HIP device: allocates
+ * the moment buffers, scales and block-descriptor table and zero-fills them
+ * (m = v = 0, scales 0: the initial state of the 8-bit Adam page).  Work is
+ * enqueued on hip_stream and the call returns after it completes.
+ * On success *out owns the state (free with adam_state_destroy).
+ * Errors: EINVAL (as adam_state_bytes, or out NULL), ENOMEM, EDEVICE.
+ */
+int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels,
+                      const adam_layout *layout, void *hip_stream);
+
+/*
+ * One Adam/AdamW step over every tensor of the state, enqueued on
+ * hip_stream as a single kernel launch (one 256-thread workgroup per
+ * 2048-element block).
+ *   params[k]: device float[numel_k], updated in place;
+ *   grads[k]:  device float[numel_k] or bf16 (uint16)[numel_k] per the
+ *              layout's grad_dtype, read only;
+ *   both arrays are host arrays of n_tensors device pointers, each 16-byte
+ *   aligned (NULL allowed only for zero-size tensors), owned by the caller
+ *   and left untouched by the library beyond the kernel's accesses.
+ *   expect: the layout the caller believes the state has; any difference
+ *   from the layout given at create returns EMODE (no work enqueued).
+ * Errors (no work enqueued): EINVAL (NULL state/params/grads/hp/expect,
+ * hyperparameter outside its domain, unknown flag bits, reserved != 0,
+ * STOCHASTIC or PERCENTILE with BF16 storage, call from a device other than
+ * the one the state was created on), EMODE, EALIGN; EDEVICE if the launch
+ * fails.  Device faults surface on the caller's next synchronization.
+ */
+int adam_step(adam_state *s, float *const *params, const void *const *grads,
+              const adam_hparams *hp, const adam_layout *expect, void *hip_stream);
+
+/* Size in bytes of one state buffer (enum adam_buffer), or < 0 if the
+   state's storage mode has no such buffer. */
+int64_t adam_state_buffer_bytes(const adam_state *s, int32_t which);
+
+/*
+ * Copies a whole state buffer to dst (device or host memory, caller-owned),
+ * or overwrites it from src, asynchronously on hip_stream; nbytes must equal
+ * adam_state_buffer_bytes(s, which).  Used for inspection, checkpoints and
+ * tests.  Errors: EINVAL (unknown/absent buffer, size mismatch, NULL
+ * pointer), EDEVICE.
+ */
+int adam_state_read(adam_state *s, int32_t which, void *dst, int64_t nbytes, void *hip_stream);
+int adam_state_write(adam_state *s, int32_t which, const void *src, int64_t nbytes,
+                     void *hip_stream);
+
+/* Frees every buffer of the state (after synchronizing the device).
+   NULL is ignored. */
+void adam_state_destroy(adam_state *s);
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char *adam_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAM_MI355X_H */

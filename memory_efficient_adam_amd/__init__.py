@@ -1,0 +1,27 @@
+"""MI355X-native compressed-moment Adam/AdamW step.
+
+Thin Python binding over ``libadam_mi355x.so`` (C ABI in
+``include/adam_mi355x.h``): the functions below carry the C names and only
+marshal arguments (torch tensors -> device pointers, the caller's current
+HIP stream).  Every step of the update runs in the library's HIP kernels;
+there is no CPU or PyTorch fallback -- if the library is not built, the
+first call raises.
+"""
+from ._binding import (  # noqa: F401
+    ADAM_BLOCK_SIZE,
+    AdamError,
+    AdamState,
+    BUFFERS,
+    GRAD_DTYPES,
+    STORAGES,
+    adam_last_error,
+    adam_state_buffer_bytes,
+    adam_state_bytes,
+    adam_state_create,
+    adam_state_destroy,
+    adam_state_read,
+    adam_state_write,
+    adam_step,
+    library,
+    library_path,
+)

@@ -1,0 +1,201 @@
+"""ctypes marshalling for libadam_mi355x.so (names follow include/adam_mi355x.h)."""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libadam_mi355x.so")
+
+ADAM_BLOCK_SIZE = 2048
+STORAGES = {"bf16": 1, "q8": 2, "q8_v_only": 3}
+GRAD_DTYPES = {"f32": 0, "bf16": 1}
+BUFFERS = {"m_codes": 0, "v_codes": 1, "m_scale": 2, "v_scale": 3, "m_bf16": 4,
+           "v_bf16": 5, "m_f32": 6}
+_F_DECOUPLED, _F_STOCHASTIC, _F_PERCENTILE = 1, 2, 4
+_STATUS = {0: "ADAM_OK", -1: "ADAM_EINVAL", -2: "ADAM_EMODE", -3: "ADAM_EALIGN",
+           -4: "ADAM_ENOMEM", -5: "ADAM_EDEVICE"}
+
+
+class adam_layout(ctypes.Structure):
+    _fields_ = [("storage", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("block_size", ctypes.c_int32)]
+
+
+class adam_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("percentile", ctypes.c_float), ("t", ctypes.c_int64),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64)]
+
+
+class AdamError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"{_STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def library():
+    """Load libadam_mi355x.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built (run __graft_entry__.build() or "
+                           "python memory_efficient_adam_amd/build.py); there is no fallback")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
+    L.adam_state_bytes.argtypes = [ctypes.c_int32, i64p, ctypes.POINTER(adam_layout)]
+    L.adam_state_bytes.restype = ctypes.c_int64
+    L.adam_state_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int32, i64p,
+                                    ctypes.POINTER(adam_layout), vp]
+    L.adam_state_create.restype = ctypes.c_int
+    L.adam_step.argtypes = [vp, vp, vp, ctypes.POINTER(adam_hparams),
+                            ctypes.POINTER(adam_layout), vp]
+    L.adam_step.restype = ctypes.c_int
+    L.adam_state_buffer_bytes.argtypes = [vp, ctypes.c_int32]
+    L.adam_state_buffer_bytes.restype = ctypes.c_int64
+    L.adam_state_read.argtypes = [vp, ctypes.c_int32, vp, ctypes.c_int64, vp]
+    L.adam_state_read.restype = ctypes.c_int
+    L.adam_state_write.argtypes = [vp, ctypes.c_int32, vp, ctypes.c_int64, vp]
+    L.adam_state_write.restype = ctypes.c_int
+    L.adam_state_destroy.argtypes = [vp]
+    L.adam_state_destroy.restype = None
+    L.adam_last_error.argtypes = []
+    L.adam_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def adam_last_error():
+    return library().adam_last_error().decode()
+
+
+def _check(rc):
+    if rc != 0:
+        raise AdamError(rc, adam_last_error())
+
+
+def _layout(storage, grad_dtype, block_size=ADAM_BLOCK_SIZE):
+    return adam_layout(STORAGES.get(storage, storage) if isinstance(storage, str) else storage,
+                       GRAD_DTYPES.get(grad_dtype, grad_dtype) if isinstance(grad_dtype, str)
+                       else grad_dtype, block_size)
+
+
+def _numels(numels):
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*[int(n) for n in numels])
+    return len(numels), arr
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def adam_state_bytes(numels, storage, grad_dtype="f32", block_size=ADAM_BLOCK_SIZE):
+    n, arr = _numels(numels)
+    lay = _layout(storage, grad_dtype, block_size)
+    rc = library().adam_state_bytes(n, arr, ctypes.byref(lay))
+    if rc < 0:
+        raise AdamError(int(rc), adam_last_error())
+    return int(rc)
+
+
+class AdamState:
+    """Owns one library state (freed on destroy() or garbage collection)."""
+
+    def __init__(self, handle, numels, layout):
+        self.handle = handle
+        self.numels = list(numels)
+        self.layout = layout
+
+    def __del__(self):
+        self.destroy()
+
+    def destroy(self):
+        if getattr(self, "handle", None):
+            library().adam_state_destroy(self.handle)
+            self.handle = None
+
+    @property
+    def storage(self):
+        return {v: k for k, v in STORAGES.items()}[self.layout.storage]
+
+
+def adam_state_create(numels, storage, grad_dtype="f32", block_size=ADAM_BLOCK_SIZE,
+                      stream=None):
+    n, arr = _numels(numels)
+    lay = _layout(storage, grad_dtype, block_size)
+    h = ctypes.c_void_p()
+    _check(library().adam_state_create(ctypes.byref(h), n, arr, ctypes.byref(lay),
+                                       _stream(stream)))
+    return AdamState(h.value, numels, lay)
+
+
+def adam_state_destroy(state):
+    state.destroy()
+
+
+def adam_step(state, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
+              decoupled=True, stochastic=False, percentile=None, seed=42, stream=None,
+              expect=None):
+    """One step over all tensors.  params: fp32 device tensors (updated in
+    place); grads: fp32 or bf16 device tensors; percentile=None selects the
+    absmax block statistic.  expect: (storage, grad_dtype[, block_size]) the
+    caller believes the state has (default: the state's own layout)."""
+    n = len(state.numels)
+    if len(params) != n or len(grads) != n:
+        raise ValueError(f"expected {n} params and grads")
+    P = (ctypes.c_void_p * max(n, 1))(*[p.data_ptr() for p in params])
+    G = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
+    flags = (_F_DECOUPLED if decoupled else 0) | (_F_STOCHASTIC if stochastic else 0) | (
+        _F_PERCENTILE if percentile is not None else 0)
+    hp = adam_hparams(lr, beta1, beta2, eps, weight_decay,
+                      100.0 if percentile is None else percentile, int(t), flags, 0, int(seed))
+    lay = state.layout if expect is None else _layout(*expect)
+    _check(library().adam_step(state.handle, ctypes.cast(P, ctypes.c_void_p),
+                               ctypes.cast(G, ctypes.c_void_p), ctypes.byref(hp),
+                               ctypes.byref(lay), _stream(stream)))
+
+
+def adam_state_buffer_bytes(state, which):
+    w = BUFFERS.get(which, which) if isinstance(which, str) else which
+    rc = library().adam_state_buffer_bytes(state.handle, w)
+    if rc < 0:
+        raise AdamError(int(rc), adam_last_error())
+    return int(rc)
+
+
+_BUF_DTYPES = {"m_codes": "int8", "v_codes": "uint8", "m_scale": "float32",
+               "v_scale": "float32", "m_bf16": "int16", "v_bf16": "int16", "m_f32": "float32"}
+
+
+def adam_state_read(state, which, out=None, stream=None):
+    """Copy a state buffer into a (new, device) torch tensor; bf16 moments
+    come back as int16 bit patterns."""
+    import torch
+    nbytes = adam_state_buffer_bytes(state, which)
+    if out is None:
+        dt = getattr(torch, _BUF_DTYPES[which])
+        out = torch.empty(nbytes // dt.itemsize, dtype=dt, device="cuda")
+    _check(library().adam_state_read(state.handle, BUFFERS[which], out.data_ptr(), nbytes,
+                                     _stream(stream)))
+    return out
+
+
+def adam_state_write(state, which, src, stream=None):
+    nbytes = adam_state_buffer_bytes(state, which)
+    if src.numel() * src.element_size() != nbytes:
+        raise ValueError("size mismatch")
+    _check(library().adam_state_write(state.handle, BUFFERS[which], src.data_ptr(), nbytes,
+                                      _stream(stream)))

@@ -1,0 +1,63 @@
+// Internal interface between the host runtime and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace adam_mi355x {
+
+constexpr int kBlock = 2048;     // elements per quantization block (8-bit Adam page default)
+constexpr int kThreads = 256;    // one workgroup per block: 4 wave64s
+constexpr int kBlockBits = 11;   // log2(kBlock)
+
+// One entry per 2048-element block, built once at create.
+//   gidx:  flat (16-padded) state index of the block's first element
+//   tensor: index into the per-tensor pointer table
+//   lb_n:  (block index within its tensor) << 11 | (elements in block - 1)
+struct BlockDesc {
+    uint64_t gidx;
+    uint32_t tensor;
+    uint32_t lb_n;
+};
+static_assert(sizeof(BlockDesc) == 16, "descriptor is one 16-byte load");
+
+// Per-tensor device pointers, refreshed when the caller's pointers change.
+struct TensorRef {
+    float *p;
+    const void *g;
+};
+static_assert(sizeof(TensorRef) == 16, "pointer pair is one 16-byte load");
+
+enum Storage : int { kStoreBf16 = 1, kStoreQ8 = 2, kStoreQ8VOnly = 3 };
+
+// Kernel arguments for one step (passed by value in the kernarg segment).
+struct StepArgs {
+    const BlockDesc *desc;
+    const TensorRef *tensors;
+    void *m_state;   // bf16 / int8 codes / fp32, per storage mode
+    void *v_state;   // bf16 / uint8 codes
+    float *m_scale;  // per block (Q8)
+    float *v_scale;  // per block (Q8, Q8_V_ONLY)
+    float step;      // lr / (1 - beta1^t)
+    float ibc2;      // 1 / sqrt(1 - beta2^t)
+    float decay;     // 1 - lr*wd (AdamW) or 1 (Adam)
+    float omb1;      // 1 - beta1
+    float omb2;      // 1 - beta2
+    float beta1, beta2, eps, wd;
+    uint32_t l2;     // 1: Adam with L2-coupled decay (g += wd*p)
+    double pfrac;    // percentile / 100 (percentile statistic)
+    uint32_t seed_lo, seed_hi, t_lo, t_hi;
+    uint32_t blk0;   // first block of this launch
+};
+
+struct Variant {
+    int storage;     // Storage
+    bool grad_bf16;
+    bool stochastic;
+    bool percentile;
+};
+
+// Enqueues the step kernel for blocks [a.blk0, a.blk0 + nblk).
+hipError_t launch_step(const Variant &v, const StepArgs &a, uint32_t nblk, hipStream_t stream);
+
+}  // namespace adam_mi355x

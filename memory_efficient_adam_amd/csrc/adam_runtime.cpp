@@ -1,0 +1,381 @@
+// Host runtime behind the C ABI declared in include/adam_mi355x.h:
+// argument validation, the padded state layout and per-block descriptor
+// table, state allocation, the per-step host scalars (fp64, rounded once --
+// the 8-bit Adam page's review comment forms the bias corrections with
+// Math.Pow on doubles) and the kernel launch on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "adam_internal.h"
+#include "adam_mi355x.h"
+
+using namespace adam_mi355x;
+
+struct adam_state {
+    int device = -1;
+    adam_layout layout{};
+    int32_t n_tensors = 0;
+    std::vector<int64_t> numels;
+    int64_t padded = 0;   // sum of pad16(numel)
+    int64_t nblocks = 0;
+    BlockDesc *d_desc = nullptr;
+    TensorRef *d_tensors = nullptr;
+    TensorRef *h_tensors = nullptr;      // pinned staging for the pointer table
+    std::vector<TensorRef> last;         // pointers the device table holds
+    bool table_valid = false;
+    hipEvent_t upload_done = nullptr;    // staging buffer reusable once this fires
+    void *m = nullptr;                   // bf16 / int8 / fp32 first moment
+    void *v = nullptr;                   // bf16 / uint8 second moment
+    float *m_scale = nullptr;
+    float *v_scale = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const std::string &msg) {
+    g_error = msg;
+    return code;
+}
+
+int64_t pad16(int64_t n) { return (n + 15) / 16 * 16; }
+
+int64_t blocks_of(int64_t n) { return (n + kBlock - 1) / kBlock; }
+
+int check_layout(const adam_layout *l) {
+    if (!l) return fail(ADAM_EINVAL, "layout is NULL");
+    if (l->storage != ADAM_STORE_BF16 && l->storage != ADAM_STORE_Q8 && l->storage != ADAM_STORE_Q8_V_ONLY)
+        return fail(ADAM_EINVAL, "unknown storage mode " + std::to_string(l->storage));
+    if (l->grad_dtype != ADAM_GRAD_F32 && l->grad_dtype != ADAM_GRAD_BF16)
+        return fail(ADAM_EINVAL, "unknown grad dtype " + std::to_string(l->grad_dtype));
+    if (l->block_size != ADAM_BLOCK_SIZE)
+        return fail(ADAM_EINVAL, "block_size must be " + std::to_string(ADAM_BLOCK_SIZE) + ", got " +
+                                     std::to_string(l->block_size));
+    return ADAM_OK;
+}
+
+int check_numels(int32_t n_tensors, const int64_t *numels) {
+    if (n_tensors < 0) return fail(ADAM_EINVAL, "n_tensors < 0");
+    if (n_tensors > 0 && !numels) return fail(ADAM_EINVAL, "numels is NULL");
+    for (int32_t k = 0; k < n_tensors; ++k)
+        if (numels[k] < 0 || numels[k] >= (int64_t(1) << 32))
+            return fail(ADAM_EINVAL, "numel of tensor " + std::to_string(k) + " outside [0, 2^32)");
+    return ADAM_OK;
+}
+
+// (bytes per padded element, bytes per block) of each storage mode
+void storage_costs(int32_t storage, int64_t &per_elem, int64_t &per_block) {
+    switch (storage) {
+    case ADAM_STORE_BF16: per_elem = 4; per_block = 0; break;
+    case ADAM_STORE_Q8: per_elem = 2; per_block = 8; break;
+    default: per_elem = 5; per_block = 4; break;
+    }
+}
+
+bool is_finite(float x) { return std::isfinite(x); }
+
+int check_hparams(const adam_hparams *hp, int32_t storage) {
+    if (!hp) return fail(ADAM_EINVAL, "hparams is NULL");
+    if (hp->t < 1) return fail(ADAM_EINVAL, "t must be >= 1");
+    if (!(hp->lr >= 0.0f) || !is_finite(hp->lr)) return fail(ADAM_EINVAL, "lr must be finite and >= 0");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f)) return fail(ADAM_EINVAL, "beta1 must be in [0, 1)");
+    if (!(hp->beta2 >= 0.0f && hp->beta2 < 1.0f)) return fail(ADAM_EINVAL, "beta2 must be in [0, 1)");
+    if (!(hp->eps > 0.0f) || !is_finite(hp->eps)) return fail(ADAM_EINVAL, "eps must be finite and > 0");
+    if (!(hp->weight_decay >= 0.0f) || !is_finite(hp->weight_decay))
+        return fail(ADAM_EINVAL, "weight_decay must be finite and >= 0");
+    const uint32_t known = ADAM_F_DECOUPLED_WD | ADAM_F_STOCHASTIC | ADAM_F_PERCENTILE;
+    if (hp->flags & ~known) return fail(ADAM_EINVAL, "unknown flag bits");
+    if (hp->reserved != 0) return fail(ADAM_EINVAL, "reserved must be 0");
+    if ((hp->flags & ADAM_F_PERCENTILE) && !(hp->percentile >= 0.0f && hp->percentile <= 100.0f))
+        return fail(ADAM_EINVAL, "percentile must be in [0, 100]");
+    if (storage == ADAM_STORE_BF16 && (hp->flags & (ADAM_F_STOCHASTIC | ADAM_F_PERCENTILE)))
+        return fail(ADAM_EINVAL, "stochastic rounding and percentile scaling apply to 8-bit storage only");
+    return ADAM_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(ADAM_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void release(adam_state *s) {
+    if (!s) return;
+    if (s->device >= 0) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        if (cur != s->device) (void)hipSetDevice(s->device);
+        (void)hipDeviceSynchronize();
+        if (s->upload_done) (void)hipEventDestroy(s->upload_done);
+        (void)hipFree(s->d_desc);
+        (void)hipFree(s->d_tensors);
+        (void)hipHostFree(s->h_tensors);
+        (void)hipFree(s->m);
+        (void)hipFree(s->v);
+        (void)hipFree(s->m_scale);
+        (void)hipFree(s->v_scale);
+        if (cur >= 0 && cur != s->device) (void)hipSetDevice(cur);
+    }
+    delete s;
+}
+
+int alloc_zeroed(void **p, int64_t bytes, hipStream_t stream) {
+    if (bytes == 0) return ADAM_OK;
+    if (hipMalloc(p, (size_t)bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        *p = nullptr;
+        return fail(ADAM_ENOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
+    }
+    hipError_t e = hipMemsetAsync(*p, 0, (size_t)bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+    return ADAM_OK;
+}
+
+struct BufferView {
+    void *ptr;
+    int64_t bytes;
+};
+
+BufferView buffer_of(const adam_state *s, int32_t which) {
+    const int32_t st = s->layout.storage;
+    switch (which) {
+    case ADAM_BUF_M_CODES: return st == ADAM_STORE_Q8 ? BufferView{s->m, s->padded} : BufferView{nullptr, -1};
+    case ADAM_BUF_V_CODES: return st != ADAM_STORE_BF16 ? BufferView{s->v, s->padded} : BufferView{nullptr, -1};
+    case ADAM_BUF_M_SCALE:
+        return st == ADAM_STORE_Q8 ? BufferView{s->m_scale, 4 * s->nblocks} : BufferView{nullptr, -1};
+    case ADAM_BUF_V_SCALE:
+        return st != ADAM_STORE_BF16 ? BufferView{s->v_scale, 4 * s->nblocks} : BufferView{nullptr, -1};
+    case ADAM_BUF_M_BF16: return st == ADAM_STORE_BF16 ? BufferView{s->m, 2 * s->padded} : BufferView{nullptr, -1};
+    case ADAM_BUF_V_BF16: return st == ADAM_STORE_BF16 ? BufferView{s->v, 2 * s->padded} : BufferView{nullptr, -1};
+    case ADAM_BUF_M_F32:
+        return st == ADAM_STORE_Q8_V_ONLY ? BufferView{s->m, 4 * s->padded} : BufferView{nullptr, -1};
+    default: return BufferView{nullptr, -1};
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *adam_last_error(void) { return g_error.c_str(); }
+
+int64_t adam_state_bytes(int32_t n_tensors, const int64_t *numels, const adam_layout *layout) {
+    int rc = check_numels(n_tensors, numels);
+    if (rc) return rc;
+    if ((rc = check_layout(layout))) return rc;
+    int64_t per_elem, per_block;
+    storage_costs(layout->storage, per_elem, per_block);
+    int64_t total = 0;
+    for (int32_t k = 0; k < n_tensors; ++k) total += pad16(numels[k]) * per_elem + blocks_of(numels[k]) * per_block;
+    return total;
+}
+
+int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels, const adam_layout *layout,
+                      void *hip_stream) {
+    if (!out) return fail(ADAM_EINVAL, "out is NULL");
+    *out = nullptr;
+    int rc = check_numels(n_tensors, numels);
+    if (rc) return rc;
+    if ((rc = check_layout(layout))) return rc;
+
+    adam_state *s = new (std::nothrow) adam_state();
+    if (!s) return fail(ADAM_ENOMEM, "host allocation failed");
+    hipError_t e = hipGetDevice(&s->device);
+    if (e != hipSuccess) {
+        s->device = -1;
+        release(s);
+        return hip_fail(e, "hipGetDevice");
+    }
+    s->layout = *layout;
+    s->n_tensors = n_tensors;
+    s->numels.assign(numels, numels + n_tensors);
+    std::vector<BlockDesc> desc;
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        const int64_t n = numels[k];
+        for (int64_t b = 0; b * kBlock < n; ++b) {
+            const int64_t len = std::min<int64_t>(kBlock, n - b * kBlock);
+            desc.push_back(BlockDesc{(uint64_t)(s->padded + b * kBlock), (uint32_t)k,
+                                     (uint32_t)((b << kBlockBits) | (len - 1))});
+        }
+        s->padded += pad16(n);
+    }
+    s->nblocks = (int64_t)desc.size();
+    if (s->nblocks >= (int64_t(1) << 32)) {
+        release(s);
+        return fail(ADAM_EINVAL, "more than 2^32 - 1 blocks");
+    }
+    s->last.assign(n_tensors, TensorRef{nullptr, nullptr});
+
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    int64_t per_elem, per_block;
+    storage_costs(layout->storage, per_elem, per_block);
+    const int32_t st = layout->storage;
+    const int64_t m_bytes = st == ADAM_STORE_BF16 ? 2 * s->padded : (st == ADAM_STORE_Q8 ? s->padded : 4 * s->padded);
+    const int64_t v_bytes = st == ADAM_STORE_BF16 ? 2 * s->padded : s->padded;
+    if ((rc = alloc_zeroed(&s->m, m_bytes, stream)) || (rc = alloc_zeroed(&s->v, v_bytes, stream))) {
+        release(s);
+        return rc;
+    }
+    if (st == ADAM_STORE_Q8 && (rc = alloc_zeroed((void **)&s->m_scale, 4 * s->nblocks, stream))) {
+        release(s);
+        return rc;
+    }
+    if (st != ADAM_STORE_BF16 && (rc = alloc_zeroed((void **)&s->v_scale, 4 * s->nblocks, stream))) {
+        release(s);
+        return rc;
+    }
+    if (s->nblocks > 0) {
+        if (hipMalloc((void **)&s->d_desc, desc.size() * sizeof(BlockDesc)) != hipSuccess) {
+            (void)hipGetLastError();
+            release(s);
+            return fail(ADAM_ENOMEM, "hipMalloc of the descriptor table failed");
+        }
+        e = hipMemcpyAsync(s->d_desc, desc.data(), desc.size() * sizeof(BlockDesc), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) {
+            release(s);
+            return hip_fail(e, "descriptor upload");
+        }
+    }
+    if (n_tensors > 0) {
+        if (hipMalloc((void **)&s->d_tensors, n_tensors * sizeof(TensorRef)) != hipSuccess ||
+            hipHostMalloc((void **)&s->h_tensors, n_tensors * sizeof(TensorRef), hipHostMallocDefault) !=
+                hipSuccess) {
+            (void)hipGetLastError();
+            release(s);
+            return fail(ADAM_ENOMEM, "pointer table allocation failed");
+        }
+    }
+    if ((e = hipEventCreateWithFlags(&s->upload_done, hipEventDisableTiming)) != hipSuccess) {
+        release(s);
+        return hip_fail(e, "hipEventCreate");
+    }
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) {
+        release(s);
+        return hip_fail(e, "hipStreamSynchronize");
+    }
+    *out = s;
+    return ADAM_OK;
+}
+
+void adam_state_destroy(adam_state *s) { release(s); }
+
+int64_t adam_state_buffer_bytes(const adam_state *s, int32_t which) {
+    if (!s) return fail(ADAM_EINVAL, "state is NULL");
+    const BufferView b = buffer_of(s, which);
+    if (b.bytes < 0) return fail(ADAM_EINVAL, "buffer " + std::to_string(which) + " absent in this storage mode");
+    return b.bytes;
+}
+
+static int copy_buffer(adam_state *s, int32_t which, void *dst, const void *src, int64_t nbytes,
+                       void *hip_stream, bool read) {
+    if (!s) return fail(ADAM_EINVAL, "state is NULL");
+    const BufferView b = buffer_of(s, which);
+    if (b.bytes < 0) return fail(ADAM_EINVAL, "buffer " + std::to_string(which) + " absent in this storage mode");
+    if (nbytes != b.bytes)
+        return fail(ADAM_EINVAL, "nbytes " + std::to_string(nbytes) + " != buffer size " + std::to_string(b.bytes));
+    if (nbytes == 0) return ADAM_OK;
+    if (read ? !dst : !src) return fail(ADAM_EINVAL, "NULL buffer pointer");
+    hipError_t e = hipMemcpyAsync(read ? dst : b.ptr, read ? b.ptr : src, (size_t)nbytes, hipMemcpyDefault,
+                                  reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    return ADAM_OK;
+}
+
+int adam_state_read(adam_state *s, int32_t which, void *dst, int64_t nbytes, void *hip_stream) {
+    return copy_buffer(s, which, dst, nullptr, nbytes, hip_stream, true);
+}
+
+int adam_state_write(adam_state *s, int32_t which, const void *src, int64_t nbytes, void *hip_stream) {
+    return copy_buffer(s, which, nullptr, src, nbytes, hip_stream, false);
+}
+
+int adam_step(adam_state *s, float *const *params, const void *const *grads, const adam_hparams *hp,
+              const adam_layout *expect, void *hip_stream) {
+    if (!s) return fail(ADAM_EINVAL, "state is NULL");
+    if (!expect) return fail(ADAM_EINVAL, "expected layout is NULL");
+    if (expect->storage != s->layout.storage || expect->grad_dtype != s->layout.grad_dtype ||
+        expect->block_size != s->layout.block_size)
+        return fail(ADAM_EMODE, "layout differs from the one the state was created with");
+    int rc = check_hparams(hp, s->layout.storage);
+    if (rc) return rc;
+    if (s->n_tensors > 0 && (!params || !grads)) return fail(ADAM_EINVAL, "params or grads is NULL");
+    for (int32_t k = 0; k < s->n_tensors; ++k) {
+        if (s->numels[k] == 0) continue;
+        if (!params[k] || !grads[k]) return fail(ADAM_EINVAL, "NULL pointer for tensor " + std::to_string(k));
+        if ((reinterpret_cast<uintptr_t>(params[k]) | reinterpret_cast<uintptr_t>(grads[k])) & 15u)
+            return fail(ADAM_EALIGN, "tensor " + std::to_string(k) + " is not 16-byte aligned");
+    }
+    if (s->nblocks == 0) return ADAM_OK;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != s->device)
+        return fail(ADAM_EINVAL, "state lives on device " + std::to_string(s->device) + ", current is " +
+                                     std::to_string(dev));
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+
+    // refresh the device pointer table when the caller's pointers changed
+    bool changed = !s->table_valid;
+    for (int32_t k = 0; k < s->n_tensors && !changed; ++k)
+        changed = s->last[k].p != params[k] || s->last[k].g != grads[k];
+    if (changed) {
+        if ((e = hipEventSynchronize(s->upload_done)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        for (int32_t k = 0; k < s->n_tensors; ++k) s->last[k] = TensorRef{params[k], grads[k]};
+        std::memcpy(s->h_tensors, s->last.data(), s->n_tensors * sizeof(TensorRef));
+        e = hipMemcpyAsync(s->d_tensors, s->h_tensors, s->n_tensors * sizeof(TensorRef), hipMemcpyHostToDevice,
+                           stream);
+        if (e != hipSuccess) {
+            s->table_valid = false;
+            return hip_fail(e, "pointer table upload");
+        }
+        if ((e = hipEventRecord(s->upload_done, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        s->table_valid = true;
+    }
+
+    // host scalars: fp64, each rounded once to fp32
+    const double b1 = hp->beta1, b2 = hp->beta2;
+    const double bc1 = 1.0 - std::pow(b1, (double)hp->t);
+    const double bc2 = 1.0 - std::pow(b2, (double)hp->t);
+    const bool decoupled = (hp->flags & ADAM_F_DECOUPLED_WD) != 0;
+    StepArgs a{};
+    a.desc = s->d_desc;
+    a.tensors = s->d_tensors;
+    a.m_state = s->m;
+    a.v_state = s->v;
+    a.m_scale = s->m_scale;
+    a.v_scale = s->v_scale;
+    a.step = (float)((double)hp->lr / bc1);
+    a.ibc2 = (float)(1.0 / std::sqrt(bc2));
+    a.decay = decoupled ? (float)(1.0 - (double)hp->lr * (double)hp->weight_decay) : 1.0f;
+    a.omb1 = (float)(1.0 - b1);
+    a.omb2 = (float)(1.0 - b2);
+    a.beta1 = hp->beta1;
+    a.beta2 = hp->beta2;
+    a.eps = hp->eps;
+    a.wd = hp->weight_decay;
+    a.l2 = decoupled ? 0u : 1u;
+    a.pfrac = (double)hp->percentile / 100.0;
+    a.seed_lo = (uint32_t)hp->seed;
+    a.seed_hi = (uint32_t)(hp->seed >> 32);
+    a.t_lo = (uint32_t)(uint64_t)hp->t;
+    a.t_hi = (uint32_t)((uint64_t)hp->t >> 32);
+
+    Variant v{s->layout.storage, s->layout.grad_dtype == ADAM_GRAD_BF16, (hp->flags & ADAM_F_STOCHASTIC) != 0,
+              (hp->flags & ADAM_F_PERCENTILE) != 0};
+    // grid.x * 256 work-items must stay below 2^32: launch in chunks
+    const int64_t kMaxBlocksPerLaunch = int64_t(1) << 23;
+    for (int64_t b0 = 0; b0 < s->nblocks; b0 += kMaxBlocksPerLaunch) {
+        a.blk0 = (uint32_t)b0;
+        const uint32_t nb = (uint32_t)std::min<int64_t>(kMaxBlocksPerLaunch, s->nblocks - b0);
+        if ((e = launch_step(v, a, nb, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
+    }
+    return ADAM_OK;
+}
+
+}  // extern "C"

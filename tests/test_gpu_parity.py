@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every test runs the library's kernels on the same seeded inputs the oracle
+gets and compares element by element (criteria in tests/parity.py):
+  * every storage mode x grad dtype x rounding x statistic on a ragged
+    multi-tensor set (16 tensors from 1 to 12289 elements: several blocks,
+    every tail shape), 10 steps, checked after every step;
+  * the 1,048,576-parameter single tensor (8-bit, nearest-even), 10 steps;
+  * the full-size ViT-Base, GPT-1.3B and Llama-7B shaped sets in the
+    benchmark's launch configuration, on a sample of blocks that includes
+    every tail block;
+  * edge cases: empty lists and zero-size tensors, a 2^32-1 element tensor,
+    injected non-zero states, degenerate hyperparameters, pointer changes,
+    a side stream, and the error paths.
+"""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import memory_efficient_adam_amd as ma
+import oracle
+import workloads
+from parity import (Stats, compare_buffer, compare_params, read_state, run_full_parity,
+                    run_sampled_parity, to_device_grads)
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+RAGGED = workloads.numels_of(workloads.ragged_shapes())
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+MODES = [
+    # storage, grad dtype, stochastic, percentile, decoupled
+    ("bf16", "f32", False, None, True),
+    ("bf16", "bf16", False, None, True),
+    ("bf16", "f32", False, None, False),
+    ("q8", "f32", False, None, True),
+    ("q8", "bf16", False, None, True),
+    ("q8", "f32", True, None, True),
+    ("q8", "bf16", True, None, True),
+    ("q8", "f32", False, 99.9, True),
+    ("q8", "bf16", True, 99.9, True),
+    ("q8", "f32", False, None, False),
+    ("q8", "f32", True, 50.0, False),
+    ("q8", "f32", False, 0.0, True),
+    ("q8", "f32", False, 100.0, True),
+    ("q8_v_only", "f32", False, None, True),
+    ("q8_v_only", "bf16", False, 99.9, True),
+    ("q8_v_only", "bf16", True, 99.9, True),
+    ("q8_v_only", "f32", True, None, False),
+]
+
+
+@pytest.mark.parametrize("storage,gdt,sr,pct,dec", MODES)
+def test_ragged_set_every_mode(storage, gdt, sr, pct, dec):
+    log(f"ragged {storage} grads={gdt} sr={sr} pct={pct} decoupled={dec}")
+    hp = dict(HP, stochastic=sr, percentile=pct, decoupled=dec, seed=1234)
+    for dist in ("normal", "student_t3"):
+        stats = run_full_parity(RAGGED, storage, gdt, 10, hp, cfg_id=11, grad_dist=dist)
+        log(f"  {dist}: {stats}")
+
+
+def test_single_tensor_1m_q8_ten_steps():
+    cfg = workloads.CONFIGS["single_q8"]
+    log("single 1M q8 nearest-even, 10 steps")
+    stats = run_full_parity(cfg.numels(), cfg.storage, cfg.grad_dtype, cfg.steps, cfg.hp,
+                            cfg_id=cfg.cfg_id)
+    log(f"  {stats}")
+    assert stats.params == 10 * 1048576
+
+
+@pytest.mark.parametrize("name", ["vit_bf16", "vit_q8", "gpt1p3b_q8_sr",
+                                  "llama7b_mf32_vq8_pct"])
+def test_full_size_sampled_blocks(name):
+    cfg = workloads.CONFIGS[name]
+    log(f"full-size {name}: {sum(cfg.numels())} params, {cfg.steps} steps")
+    stats = run_sampled_parity(cfg, log=log)
+    # every step compared at least the sampled blocks' params (and codes)
+    assert stats.params >= cfg.steps * 800 * 1024
+    if cfg.storage != "bf16":
+        assert stats.codes >= stats.params
+
+
+def test_empty_and_zero_size_tensors():
+    st = ma.adam_state_create([], "q8")
+    ma.adam_step(st, [], [], t=1, **HP)
+    st.destroy()
+    numels = [0, 5, 0, 3000, 0]
+    run_full_parity(numels, "q8", "f32", 3, dict(HP, stochastic=True), cfg_id=12)
+    run_full_parity(numels, "bf16", "bf16", 3, HP, cfg_id=12)
+    st = ma.adam_state_create([0, 0], "bf16")
+    z = torch.empty(0, device="cuda")
+    ma.adam_step(st, [z, z], [z, z], t=1, **HP)
+    st.destroy()
+
+
+def test_largest_tensor_last_blocks():
+    # numel 2^32 - 1: the largest tensor the descriptor format takes
+    n = 2 ** 32 - 1
+    log("2^32-1 element tensor, q8 with bf16 grads, 2 steps (last 3 blocks checked)")
+    p = torch.empty(n, dtype=torch.float32, device="cuda")
+    g = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    p.normal_(0, 0.02, generator=gen)
+    tail = 2048 * 2 + (n % 2048)
+    lo = n - tail
+    host_p = [p[lo:].cpu().numpy()]
+    st = ma.adam_state_create([n], "q8", "bf16")
+    first_block = lo // 2048
+    ob = oracle.OracleBlocks([(2048, lo), (2048, lo + 2048), (n % 2048, lo + 4096)], "q8",
+                             grad_bf16=True)
+    stats = Stats()
+    for t in (1, 2):
+        g.normal_(0, 1e-3, generator=gen)
+        hg = g[lo:].view(torch.int16).cpu().numpy().view(np.uint16)
+        ma.adam_step(st, [p], [g], t=t, stochastic=True, seed=99, **HP)
+        blocks_p = [host_p[0][0:2048], host_p[0][2048:4096], host_p[0][4096:]]
+        ob.step(blocks_p, [hg[0:2048], hg[2048:4096], hg[4096:]], t=t, stochastic=True,
+                seed=99, **HP)
+        host_p = [np.concatenate(blocks_p)]
+        torch.cuda.synchronize()
+        compare_params(p[lo:].cpu().numpy(), host_p[0], stats, f"t={t}")
+        codes = ma.adam_state_read(st, "m_codes")
+        compare_buffer("m_codes", codes[lo:n].cpu().numpy(),
+                       np.concatenate([ob.inner.m_codes[ob.block_slice(i)] for i in range(3)]),
+                       True, stats, f"t={t}")
+        del codes
+        sc = ma.adam_state_read(st, "v_scale")[first_block:].cpu().numpy()
+        compare_buffer("v_scale", sc, ob.inner.v_scale, True, stats, f"t={t}")
+    log(f"  {stats}")
+    st.destroy()
+    del p, g
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("storage", ["bf16", "q8", "q8_v_only"])
+def test_step_from_injected_state(storage):
+    # arbitrary (non-trajectory) state: extreme codes, tiny / huge / zero scales
+    numels = [2048, 5000, 17]
+    rng = np.random.default_rng(21)
+    ost = oracle.OracleState(numels, storage)
+    for name, buf in ost.buffers().items():
+        if name == "m_codes":
+            buf[:] = rng.integers(-127, 128, buf.size)
+        elif name == "v_codes":
+            buf[:] = rng.integers(0, 256, buf.size)
+        elif name.endswith("scale"):
+            buf[:] = (10.0 ** rng.uniform(-30, 2, buf.size)).astype(np.float32)
+            buf[0] = 0.0
+            buf[-1] = np.float32(2.0 ** -112)
+        elif name.endswith("bf16"):
+            x = (rng.standard_normal(buf.size) * 1e-3).astype(np.float32)
+            buf[:] = oracle.bf16_from_f32(np.abs(x) if name == "v_bf16" else x)
+        elif name == "m_f32":
+            buf[:] = (rng.standard_normal(buf.size) * 1e-3).astype(np.float32)
+    # padding entries stay zero, as the layout keeps them
+    seg = 0
+    for n in numels:
+        for name, buf in ost.buffers().items():
+            if not name.endswith("scale"):
+                buf[seg + n:seg + oracle.pad16(n)] = 0
+        seg += oracle.pad16(n)
+    st = ma.adam_state_create(numels, storage)
+    for name, buf in ost.buffers().items():
+        src = torch.from_numpy(buf.view(np.int16) if name.endswith("bf16") else buf).cuda()
+        ma.adam_state_write(st, name, src)
+    params = workloads.host_params(22, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    stats = Stats()
+    for t in (7, 8):
+        grads = workloads.host_grads(22, numels, t)
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **HP)
+        ost.step(params, grads, t=t, **HP)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats)
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, False, stats, f"t={t}")
+    st.destroy()
+
+
+@pytest.mark.parametrize("case", ["beta1_zero", "lr_zero", "wd_zero", "late_step", "big_eps",
+                                  "zero_grads", "constant_grads", "tiny_grads"])
+def test_degenerate_hyperparameters(case):
+    hp = dict(HP)
+    numels = [4100, 2048, 31]
+    params = workloads.host_params(23, numels)
+    t0 = 1
+    if case == "beta1_zero":
+        hp["beta1"] = 0.0
+    elif case == "lr_zero":
+        hp["lr"] = 0.0
+    elif case == "wd_zero":
+        hp["weight_decay"] = 0.0
+    elif case == "late_step":
+        t0 = 10 ** 6
+    elif case == "big_eps":
+        hp["eps"] = 1.0
+    for storage, sr in (("bf16", False), ("q8", False), ("q8", True), ("q8_v_only", False)):
+        p = [x.copy() for x in params]
+        dev_p = [torch.from_numpy(x.copy()).cuda() for x in p]
+        st = ma.adam_state_create(numels, storage)
+        ost = oracle.OracleState(numels, storage)
+        stats = Stats()
+        for t in range(t0, t0 + 3):
+            if case == "zero_grads":
+                grads = [np.zeros(n, np.float32) for n in numels]
+            elif case == "constant_grads":
+                grads = [np.full(n, np.float32(3e-4 * (-1) ** t), np.float32) for n in numels]
+            elif case == "tiny_grads":
+                grads = [(g * np.float32(1e-20)).astype(np.float32)
+                         for g in workloads.host_grads(23, numels, t)]
+            else:
+                grads = workloads.host_grads(23, numels, t)
+            ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, stochastic=sr, **hp)
+            ost.step(p, grads, t=t, stochastic=sr, **hp)
+            torch.cuda.synchronize()
+            for k in range(len(numels)):
+                compare_params(dev_p[k].cpu().numpy(), p[k], stats, f"{case} {storage} t={t}")
+            got = read_state(st)
+            for nm, want in ost.buffers().items():
+                compare_buffer(nm, got[nm], want, sr, stats, f"{case} {storage} t={t}")
+        st.destroy()
+
+
+def test_pointer_change_and_side_stream():
+    numels = [3000, 2048]
+    params = workloads.host_params(24, numels)
+    st = ma.adam_state_create(numels, "q8")
+    ost = oracle.OracleState(numels, "q8")
+    side = torch.cuda.Stream()
+    stats = Stats()
+    dev_p = [torch.from_numpy(x.copy()).cuda() for x in params]
+    for t in range(1, 5):
+        grads = workloads.host_grads(24, numels, t)
+        if t == 3:  # move the params to new allocations
+            dev_p = [x.clone() for x in dev_p]
+        dg = to_device_grads(grads, "f32")
+        if t % 2:
+            ma.adam_step(st, dev_p, dg, t=t, **HP)
+        else:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                ma.adam_step(st, dev_p, dg, t=t, **HP)
+            torch.cuda.current_stream().wait_stream(side)
+        ost.step(params, grads, t=t, **HP)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats)
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, False, stats)
+    st.destroy()
+
+
+def test_two_states_interleaved():
+    a_n, b_n = [5000], [2049, 7]
+    pa = workloads.host_params(25, a_n)
+    pb = workloads.host_params(26, b_n)
+    sa, sb = ma.adam_state_create(a_n, "q8"), ma.adam_state_create(b_n, "bf16", "bf16")
+    oa, ob = oracle.OracleState(a_n, "q8"), oracle.OracleState(b_n, "bf16", grad_bf16=True)
+    da = [torch.from_numpy(x.copy()).cuda() for x in pa]
+    db = [torch.from_numpy(x.copy()).cuda() for x in pb]
+    for t in (1, 2, 3):
+        ga = workloads.host_grads(25, a_n, t)
+        gb = workloads.host_grads(26, b_n, t, dtype="bf16")
+        ma.adam_step(sa, da, to_device_grads(ga, "f32"), t=t, **HP)
+        ma.adam_step(sb, db, to_device_grads(gb, "bf16"), t=t, **HP)
+        oa.step(pa, ga, t=t, **HP)
+        ob.step(pb, gb, t=t, **HP)
+    torch.cuda.synchronize()
+    stats = Stats()
+    for d, h in zip(da + db, pa + pb):
+        compare_params(d.cpu().numpy(), h, stats)
+    for st, o in ((sa, oa), (sb, ob)):
+        got = read_state(st)
+        for nm, want in o.buffers().items():
+            compare_buffer(nm, got[nm], want, False, stats)
+    sa.destroy()
+    sb.destroy()
+
+
+def test_error_paths_enqueue_nothing():
+    numels = [100]
+    st = ma.adam_state_create(numels, "q8")
+    p = torch.zeros(104, device="cuda")
+    g = torch.zeros(104, device="cuda")
+    before = p.clone()
+    with pytest.raises(ma.AdamError) as e:  # layout drift
+        ma.adam_step(st, [p[:100]], [g[:100]], t=1, expect=("bf16", "f32"), **HP)
+    assert e.value.code == -2
+    with pytest.raises(ma.AdamError) as e:  # 4-byte offset pointer
+        ma.adam_step(st, [p[1:101]], [g[:100]], t=1, **HP)
+    assert e.value.code == -3
+    for bad in (dict(t=0), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(lr=-1.0),
+                dict(weight_decay=float("nan")), dict(percentile=101.0)):
+        kw = dict(HP, t=1)
+        kw.update(bad)
+        with pytest.raises(ma.AdamError) as e:
+            ma.adam_step(st, [p[:100]], [g[:100]], **kw)
+        assert e.value.code == -1, bad
+    bst = ma.adam_state_create(numels, "bf16")
+    with pytest.raises(ma.AdamError):
+        ma.adam_step(bst, [p[:100]], [g[:100]], t=1, stochastic=True, **HP)
+    with pytest.raises(ma.AdamError):
+        ma.adam_state_read(bst, "m_codes")
+    lib = ma.library()
+    buf = torch.empty(10, dtype=torch.uint8, device="cuda")
+    assert lib.adam_state_read(ctypes.c_void_p(st.handle), 1, ctypes.c_void_p(buf.data_ptr()), 10,
+                               None) == -1
+    torch.cuda.synchronize()
+    assert torch.equal(p, before)
+    st.destroy()
+    bst.destroy()
