@@ -35,6 +35,38 @@ constexpr int kGroups = kBlock / (kThreads * 4);  // 4-element groups per thread
 constexpr int kItems = kGroups * 4;               // elements per thread (8)
 constexpr float kTiny = 0x1p-112f;                // smallest block statistic encoded
 
+// ---------------------------------------------------------------- streaming access
+// Every byte of params, grads and state is touched exactly once per step, so
+// all data accesses are non-temporal (the "nt" cache policy): measured on
+// MI355X this raises the mixed read/write stream rate by 5-10% over the
+// default policy, and only when loads and stores both use it.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 ld_f32x4(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+__device__ __forceinline__ u32x2 ld_u32x2(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+__device__ __forceinline__ uint32_t ld_u32(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+template <class T>
+__device__ __forceinline__ T ld_one(const T *p) {
+    return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ void st_f32x4(float *p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ void st_u32x2(void *p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+}
+__device__ __forceinline__ void st_u32(void *p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(p));
+}
+__device__ __forceinline__ void st_one(float *p, float v) { __builtin_nontemporal_store(v, p); }
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -179,29 +211,27 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
     for (int j = 0; j < kGroups; ++j) {
         const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
         if (e0 + 4 <= n) {
-            const float4 x = *reinterpret_cast<const float4 *>(pp + e0);
+            const f32x4 x = ld_f32x4(pp + e0);
             p[4 * j + 0] = x.x; p[4 * j + 1] = x.y; p[4 * j + 2] = x.z; p[4 * j + 3] = x.w;
             if constexpr (kGradBf16) {
-                const uint2 h = *reinterpret_cast<const uint2 *>(
-                    reinterpret_cast<const uint16_t *>(tr.g) + local + e0);
+                const u32x2 h = ld_u32x2(reinterpret_cast<const uint16_t *>(tr.g) + local + e0);
                 g[4 * j + 0] = bf16_to_f32(h.x & 0xFFFFu);
                 g[4 * j + 1] = bf16_to_f32(h.x >> 16);
                 g[4 * j + 2] = bf16_to_f32(h.y & 0xFFFFu);
                 g[4 * j + 3] = bf16_to_f32(h.y >> 16);
             } else {
-                const float4 y = *reinterpret_cast<const float4 *>(
-                    reinterpret_cast<const float *>(tr.g) + local + e0);
+                const f32x4 y = ld_f32x4(reinterpret_cast<const float *>(tr.g) + local + e0);
                 g[4 * j + 0] = y.x; g[4 * j + 1] = y.y; g[4 * j + 2] = y.z; g[4 * j + 3] = y.w;
             }
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const bool in = e0 + c < n;
-                p[4 * j + c] = in ? pp[e0 + c] : 0.0f;
+                p[4 * j + c] = in ? ld_one(pp + e0 + c) : 0.0f;
                 if constexpr (kGradBf16)
-                    g[4 * j + c] = in ? bf16_to_f32(reinterpret_cast<const uint16_t *>(tr.g)[local + e0 + c]) : 0.0f;
+                    g[4 * j + c] = in ? bf16_to_f32(ld_one(reinterpret_cast<const uint16_t *>(tr.g) + local + e0 + c)) : 0.0f;
                 else
-                    g[4 * j + c] = in ? reinterpret_cast<const float *>(tr.g)[local + e0 + c] : 0.0f;
+                    g[4 * j + c] = in ? ld_one(reinterpret_cast<const float *>(tr.g) + local + e0 + c) : 0.0f;
             }
         }
     }
@@ -218,10 +248,10 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
         const size_t s = d.gidx + e0;
         const bool in = e0 < npad;
         if constexpr (kStore == kStoreBf16) {
-            uint2 hm = make_uint2(0, 0), hv = make_uint2(0, 0);
+            u32x2 hm = {0u, 0u}, hv = {0u, 0u};
             if (in) {
-                hm = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.m_state) + s);
-                hv = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.v_state) + s);
+                hm = ld_u32x2(reinterpret_cast<const uint16_t *>(a.m_state) + s);
+                hv = ld_u32x2(reinterpret_cast<const uint16_t *>(a.v_state) + s);
             }
             mo[4 * j + 0] = bf16_to_f32(hm.x & 0xFFFFu); mo[4 * j + 1] = bf16_to_f32(hm.x >> 16);
             mo[4 * j + 2] = bf16_to_f32(hm.y & 0xFFFFu); mo[4 * j + 3] = bf16_to_f32(hm.y >> 16);
@@ -229,20 +259,20 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
             vo[4 * j + 2] = bf16_to_f32(hv.y & 0xFFFFu); vo[4 * j + 3] = bf16_to_f32(hv.y >> 16);
         } else {
             uint32_t cv = 0;
-            if (in) cv = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(a.v_state) + s);
+            if (in) cv = ld_u32(reinterpret_cast<const uint8_t *>(a.v_state) + s);
 #pragma unroll
             for (int c = 0; c < 4; ++c) vo[4 * j + c] = ((float)((cv >> (8 * c)) & 0xFFu) * Rv) * Av;
             if constexpr (kQuantM) {
                 uint32_t cm = 0;
-                if (in) cm = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const int8_t *>(a.m_state) + s);
+                if (in) cm = ld_u32(reinterpret_cast<const int8_t *>(a.m_state) + s);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int32_t q = ((int32_t)(cm << (24 - 8 * c))) >> 24;
                     mo[4 * j + c] = ((float)q * Rm) * Am;
                 }
             } else {
-                float4 mf = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (in) mf = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.m_state) + s);
+                f32x4 mf = {0.f, 0.f, 0.f, 0.f};
+                if (in) mf = ld_f32x4(reinterpret_cast<const float *>(a.m_state) + s);
                 mo[4 * j + 0] = mf.x; mo[4 * j + 1] = mf.y; mo[4 * j + 2] = mf.z; mo[4 * j + 3] = mf.w;
             }
         }
@@ -269,11 +299,11 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
     for (int j = 0; j < kGroups; ++j) {
         const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
         if (e0 + 4 <= n) {
-            *reinterpret_cast<float4 *>(pp + e0) = make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+            st_f32x4(pp + e0, f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]});
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (e0 + c < n) pp[e0 + c] = p[4 * j + c];
+                if (e0 + c < n) st_one(pp + e0 + c, p[4 * j + c]);
         }
     }
 
@@ -283,13 +313,12 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
             const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
             if (e0 < npad) {
                 const size_t s = d.gidx + e0;
-                uint2 hm, hv;
-                hm.x = f32_to_bf16(mo[4 * j]) | (f32_to_bf16(mo[4 * j + 1]) << 16);
-                hm.y = f32_to_bf16(mo[4 * j + 2]) | (f32_to_bf16(mo[4 * j + 3]) << 16);
-                hv.x = f32_to_bf16(vo[4 * j]) | (f32_to_bf16(vo[4 * j + 1]) << 16);
-                hv.y = f32_to_bf16(vo[4 * j + 2]) | (f32_to_bf16(vo[4 * j + 3]) << 16);
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.m_state) + s) = hm;
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.v_state) + s) = hv;
+                const u32x2 hm = {f32_to_bf16(mo[4 * j]) | (f32_to_bf16(mo[4 * j + 1]) << 16),
+                                  f32_to_bf16(mo[4 * j + 2]) | (f32_to_bf16(mo[4 * j + 3]) << 16)};
+                const u32x2 hv = {f32_to_bf16(vo[4 * j]) | (f32_to_bf16(vo[4 * j + 1]) << 16),
+                                  f32_to_bf16(vo[4 * j + 2]) | (f32_to_bf16(vo[4 * j + 3]) << 16)};
+                st_u32x2(reinterpret_cast<uint16_t *>(a.m_state) + s, hm);
+                st_u32x2(reinterpret_cast<uint16_t *>(a.v_state) + s, hv);
             }
         }
         return;
@@ -339,7 +368,7 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
                                       : code_magnitude<kSR>(fabsf(vo[4 * j + c]), Avn, rv, 255.0f, w[c] >> 16);
                 cv |= ((uint32_t)k) << (8 * c);
             }
-            *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(a.v_state) + s) = cv;
+            st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s, cv);
             if constexpr (kQuantM) {
                 uint32_t cm = 0;
 #pragma unroll
@@ -350,10 +379,10 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
                     const int32_t q = x < 0.0f ? -(int32_t)k : (int32_t)k;
                     cm |= ((uint32_t)q & 0xFFu) << (8 * c);
                 }
-                *reinterpret_cast<uint32_t *>(reinterpret_cast<int8_t *>(a.m_state) + s) = cm;
+                st_u32(reinterpret_cast<int8_t *>(a.m_state) + s, cm);
             } else {
-                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.m_state) + s) =
-                    make_float4(mo[4 * j], mo[4 * j + 1], mo[4 * j + 2], mo[4 * j + 3]);
+                st_f32x4(reinterpret_cast<float *>(a.m_state) + s,
+                         f32x4{mo[4 * j], mo[4 * j + 1], mo[4 * j + 2], mo[4 * j + 3]});
             }
         }
         if (tid == 0) {
