@@ -24,7 +24,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "memory_efficient_adam_amd", "csrc", "adam_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "memory_efficient_adam_amd", "csrc", f)
+                  for f in ("adam_kernels.hip", "adam_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 # algorithmic bytes per parameter (read + write) and per block (scales)
@@ -43,8 +44,12 @@ def algorithmic_bytes(cfg):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the sources that define the step kernel."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_for(workload):

@@ -10,14 +10,18 @@ constexpr int kBlock = 2048;     // elements per quantization block (8-bit Adam 
 constexpr int kThreads = 256;    // one workgroup per block: 4 wave64s
 constexpr int kBlockBits = 11;   // log2(kBlock)
 
-// One entry per 2048-element block, built once at create.
-//   gidx:  flat (16-padded) state index of the block's first element
+// One entry per 2048-element block, built once at create.  The table lists
+// the full (2048-element) blocks first and the ragged last blocks of the
+// tensors after them, so the hot loop over full blocks has no tail checks.
+//   gidx16: flat (16-padded) state index of the block's first element / 16
 //   tensor: index into the per-tensor pointer table
-//   lb_n:  (block index within its tensor) << 11 | (elements in block - 1)
+//   lb_n:   (block index within its tensor) << 11 | (elements in block - 1)
+//   slot:   the block's scale slot (blocks numbered tensor-major)
 struct BlockDesc {
-    uint64_t gidx;
+    uint32_t gidx16;
     uint32_t tensor;
     uint32_t lb_n;
+    uint32_t slot;
 };
 static_assert(sizeof(BlockDesc) == 16, "descriptor is one 16-byte load");
 
@@ -47,7 +51,8 @@ struct StepArgs {
     uint32_t l2;     // 1: Adam with L2-coupled decay (g += wd*p)
     double pfrac;    // percentile / 100 (percentile statistic)
     uint32_t seed_lo, seed_hi, t_lo, t_hi;
-    uint32_t blk0;   // first block of this launch
+    uint32_t n_full;   // descriptors [0, n_full) are full blocks
+    uint32_t n_all;    // descriptors [n_full, n_all) are ragged last blocks
 };
 
 struct Variant {
@@ -57,7 +62,7 @@ struct Variant {
     bool percentile;
 };
 
-// Enqueues the step kernel for blocks [a.blk0, a.blk0 + nblk).
-hipError_t launch_step(const Variant &v, const StepArgs &a, uint32_t nblk, hipStream_t stream);
+// Enqueues the step kernel over every descriptor.
+hipError_t launch_step(const Variant &v, const StepArgs &a, hipStream_t stream);
 
 }  // namespace adam_mi355x

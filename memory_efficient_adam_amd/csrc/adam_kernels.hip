@@ -3,9 +3,9 @@
 // One 256-thread workgroup (4 wave64s) owns one 2048-element block: it
 // reads the block's params, grads, stored moments and old scales once,
 // keeps the updated moments in registers, reduces the block statistic
-// (wave shuffles + a cross-wave LDS step; an LDS radix select for the
-// percentile statistic), requantizes and writes params, moments and the new
-// scales once.  The step is a streaming map over HBM (14-20 bytes per
+// (DPP cross-lane steps + one cross-wave LDS step; an LDS radix select for
+// the percentile statistic), requantizes and writes params, moments and the
+// new scales once.  The step is a streaming map over HBM (14-20 bytes per
 // parameter, ~1.5 flop/byte), so there is no MFMA work; what matters is
 // coalesced 16-byte loads, enough bytes in flight per CU and a VALU budget
 // of roughly 100 instructions per element at the bandwidth target.
@@ -24,6 +24,8 @@
 // contiguous span (1 KiB of fp32 per wave per instruction).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "adam_internal.h"
 
@@ -81,33 +83,60 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint32_t lo0 = 0xD2511F53u * c[0];
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]);
-        const uint32_t lo1 = 0xCD9E8D57u * c[2];
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]);
-        c[0] = hi1 ^ c[1] ^ k0;
-        c[1] = lo1;
-        c[2] = hi0 ^ c[3] ^ k1;
-        c[3] = lo0;
+        // one 32x32->64 multiply each (v_mad_u64_u32) instead of separate hi/lo
+        const uint64_t prod0 = (uint64_t)0xD2511F53u * c[0];
+        const uint64_t prod1 = (uint64_t)0xCD9E8D57u * c[2];
+        c[0] = (uint32_t)(prod1 >> 32) ^ c[1] ^ k0;
+        c[1] = (uint32_t)prod1;
+        c[2] = (uint32_t)(prod0 >> 32) ^ c[3] ^ k1;
+        c[3] = (uint32_t)prod0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
 }
 
 // ---------------------------------------------------------------- reductions
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-    return x;
+// Cross-lane steps use DPP (data-parallel primitives: a VALU operand taken
+// from another lane of the same row, or broadcast between rows), a few cycles
+// each, instead of LDS-routed lane shuffles.  Lanes a DPP step does not
+// write read 0, the identity of both the max of non-negative values and the
+// sum below.
+template <int kCtrl, int kRowMask = 0xF, int kBankMask = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, kBankMask, false);
+}
+constexpr int kQuadPerm1032 = 0xB1;  // lanes 1,0,3,2 of each quad
+constexpr int kQuadPerm2301 = 0x4E;  // lanes 2,3,0,1 of each quad
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr3 = 0x113, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+__device__ __forceinline__ float fmax_dpp_row(float x) {
+    x = fmaxf(x, __uint_as_float(dpp<kQuadPerm1032>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp<kQuadPerm2301>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp<kRowRor4>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp<kRowRor8>(__float_as_uint(x))));
+    return x;  // every lane holds its row's max
 }
 
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
+// Max over the wave of non-negative values, as a wave-uniform value.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmax_dpp_row(x);
+    x = fmaxf(x, __uint_as_float(dpp<kRowBcast15, 0xA>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp<kRowBcast31, 0xC>(__float_as_uint(x))));
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), 63));
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    uint32_t v = x + dpp<kRowShr1>(x);
+    v += dpp<kRowShr2>(x);
+    v += dpp<kRowShr3>(x);              // v = sum of lanes i-3..i of the row
+    v += dpp<kRowShr4, 0xF, 0xE>(v);    // lanes 4..15: i-7..i
+    v += dpp<kRowShr8, 0xF, 0xC>(v);    // lanes 8..15: whole row prefix
+    v += dpp<kRowBcast15, 0xA>(v);      // rows 1, 3 add the previous row's total
+    v += dpp<kRowBcast31, 0xC>(v);      // rows 2, 3 add the total of rows 0..1
+    return v;
 }
 
 // Block-wide max of two non-negative values (one barrier).
@@ -115,6 +144,7 @@ __device__ __forceinline__ void block_max2(float &a, float &b, float (*red)[kWav
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     a = wave_max(a);
     b = wave_max(b);
+    if (kWaves == 1) return;
     if (lane == 0) {
         red[0][wave] = a;
         red[1][wave] = b;
@@ -135,6 +165,7 @@ __device__ __forceinline__ void block_max2(float &a, float &b, float (*red)[kWav
 __device__ uint32_t block_select(const uint32_t (&key)[kItems], uint32_t rank, uint32_t *hist,
                                  uint32_t *scratch) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    (void)lane;
     uint32_t prefix = 0, pmask = 0;
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
@@ -150,7 +181,7 @@ __device__ uint32_t block_select(const uint32_t (&key)[kItems], uint32_t rank, u
         __syncthreads();
         uint32_t mine = 0;
         for (int i = 0; i < per; ++i) mine += hist[tid * per + i];
-        uint32_t incl = wave_inclusive_sum(mine, lane);
+        uint32_t incl = wave_inclusive_sum(mine);
         if (lane == 63) scratch[wave] = incl;
         __syncthreads();
         for (int w = 0; w < wave; ++w) incl += scratch[w];
@@ -173,9 +204,13 @@ __device__ uint32_t block_select(const uint32_t (&key)[kItems], uint32_t rank, u
 
 // ---------------------------------------------------------------- quantizer
 // Code magnitude for |x| = a with statistic A and r = fl(qmax/A) (A >= kTiny).
-template <bool kSR>
+// With the absmax statistic and nearest-even rounding, a <= A always holds and
+// r = (qmax/A)(1+d), |d| <= 2^-24, so fl(a*r) <= qmax*(1 + 2^-23) and rounds to
+// at most qmax, reaching it at a = A: the end pin and the clamp are then no-ops
+// and are skipped (kClip = false).  Percentile statistics (a may exceed A) and
+// stochastic rounding (floor of a value just below qmax) keep both.
+template <bool kSR, bool kClip>
 __device__ __forceinline__ float code_magnitude(float a, float A, float r, float qmax, uint32_t u16) {
-    if (a >= A) return qmax;
     const float y = a * r;
     float k;
     if constexpr (kSR) {
@@ -186,104 +221,183 @@ __device__ __forceinline__ float code_magnitude(float a, float A, float r, float
     } else {
         k = rintf(y);
     }
-    return fminf(k, qmax);
+    if constexpr (kClip) {
+        k = fminf(k, qmax);
+        k = a >= A ? qmax : k;
+    }
+    return k;
 }
 
-template <int kStore, bool kGradBf16, bool kSR, bool kPct>
-__global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
-    constexpr bool kQuantM = (kStore == kStoreQ8);
-    constexpr bool kQuantV = (kStore != kStoreBf16);
+// ---------------------------------------------------------------- one block
+// Scalars of one block: where its data lives and its stored scales.
+struct BlockCtx {
+    uint64_t gidx;   // flat state index of the block's first element
+    float *p;        // the block's params
+    const void *g;   // the block's grads
+    uint32_t n;      // live elements (1..2048)
+    uint32_t npad;   // n rounded up to 16 (state entries owned by the block)
+    uint32_t slot;   // scale slot
+};
 
-    const uint32_t blk = a.blk0 + blockIdx.x;
-    const BlockDesc d = a.desc[blk];
-    const TensorRef tr = a.tensors[d.tensor];
-    const uint32_t n = (d.lb_n & (kBlock - 1)) + 1u;
-    const uint32_t npad = (n + 15u) & ~15u;
-    const size_t local = (size_t)(d.lb_n >> kBlockBits) * kBlock;
+// The descriptor and pointer tables do not change during a launch: reading
+// them through the constant address space lets them be scalar loads even
+// after the kernel's own stores (a generic load there would be a vector load
+// whose wait also drains every prefetched data load).
+typedef const __attribute__((address_space(4))) BlockDesc *ConstDescPtr;
+typedef const __attribute__((address_space(4))) TensorRef *ConstTensorPtr;
+
+template <bool kGradBf16>
+__device__ __forceinline__ BlockCtx load_ctx(const StepArgs &a, uint32_t idx) {
+    const ConstDescPtr d = (ConstDescPtr)a.desc + idx;
+    const uint32_t lb_n = d->lb_n;
+    const ConstTensorPtr tr = (ConstTensorPtr)a.tensors + d->tensor;
+    const size_t local = (size_t)(lb_n >> kBlockBits) * kBlock;
+    BlockCtx c;
+    c.gidx = (uint64_t)d->gidx16 * 16u;
+    c.p = tr->p + local;
+    c.g = kGradBf16 ? (const void *)(reinterpret_cast<const uint16_t *>(tr->g) + local)
+                    : (const void *)(reinterpret_cast<const float *>(tr->g) + local);
+    c.n = (lb_n & (kBlock - 1)) + 1u;
+    c.npad = (c.n + 15u) & ~15u;
+    c.slot = d->slot;
+    return c;
+}
+
+// Raw (undecoded) per-thread data of one block, as loaded.
+template <int kStore, bool kGradBf16>
+struct BlockRegs {
+    float p[kItems];
+    uint32_t g[kGradBf16 ? kItems / 2 : kItems];  // fp32 bits, or bf16 pairs
+    uint32_t m[kStore == kStoreBf16 ? kItems / 2 : (kStore == kStoreQ8 ? kGroups : kItems)];
+    uint32_t v[kStore == kStoreBf16 ? kItems / 2 : kGroups];
+    float Am, Av;  // stored scales of the 8-bit moments
+};
+
+// Issues every load of one block.  kFull: the block has 2048 live elements,
+// so all loads are unconditional 16/8/4-byte vector loads (no branches: the
+// compiler's wait counts then let the loads stay in flight across the
+// previous block's compute).  Otherwise the ragged last group uses element
+// loads and state slots past the tensor's padded segment are not touched.
+template <int kStore, bool kGradBf16, bool kFull>
+__device__ __forceinline__ void load_data(const StepArgs &a, const BlockCtx &c,
+                                          BlockRegs<kStore, kGradBf16> &r) {
     const int tid = threadIdx.x;
-
-    float *__restrict__ pp = tr.p + local;
-
-    float p[kItems], g[kItems], mo[kItems], vo[kItems];
-
-    // ---- load params and grads (vector loads; element loads in a ragged tail group)
+    r.Am = kStore == kStoreQ8 ? a.m_scale[c.slot] : 0.0f;
+    r.Av = kStore != kStoreBf16 ? a.v_scale[c.slot] : 0.0f;
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
         const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
-        if (e0 + 4 <= n) {
-            const f32x4 x = ld_f32x4(pp + e0);
-            p[4 * j + 0] = x.x; p[4 * j + 1] = x.y; p[4 * j + 2] = x.z; p[4 * j + 3] = x.w;
+        if (kFull || e0 + 4 <= c.n) {
+            const f32x4 x = ld_f32x4(c.p + e0);
+            r.p[4 * j + 0] = x.x; r.p[4 * j + 1] = x.y; r.p[4 * j + 2] = x.z; r.p[4 * j + 3] = x.w;
             if constexpr (kGradBf16) {
-                const u32x2 h = ld_u32x2(reinterpret_cast<const uint16_t *>(tr.g) + local + e0);
-                g[4 * j + 0] = bf16_to_f32(h.x & 0xFFFFu);
-                g[4 * j + 1] = bf16_to_f32(h.x >> 16);
-                g[4 * j + 2] = bf16_to_f32(h.y & 0xFFFFu);
-                g[4 * j + 3] = bf16_to_f32(h.y >> 16);
+                const u32x2 h = ld_u32x2(reinterpret_cast<const uint16_t *>(c.g) + e0);
+                r.g[2 * j] = h.x;
+                r.g[2 * j + 1] = h.y;
             } else {
-                const f32x4 y = ld_f32x4(reinterpret_cast<const float *>(tr.g) + local + e0);
-                g[4 * j + 0] = y.x; g[4 * j + 1] = y.y; g[4 * j + 2] = y.z; g[4 * j + 3] = y.w;
+                const f32x4 y = ld_f32x4(reinterpret_cast<const float *>(c.g) + e0);
+                r.g[4 * j + 0] = __float_as_uint(y.x); r.g[4 * j + 1] = __float_as_uint(y.y);
+                r.g[4 * j + 2] = __float_as_uint(y.z); r.g[4 * j + 3] = __float_as_uint(y.w);
             }
         } else {
+            // ragged last group: element loads, zeros past the tensor's end
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bool in = e0 + c < n;
-                p[4 * j + c] = in ? ld_one(pp + e0 + c) : 0.0f;
-                if constexpr (kGradBf16)
-                    g[4 * j + c] = in ? bf16_to_f32(ld_one(reinterpret_cast<const uint16_t *>(tr.g) + local + e0 + c)) : 0.0f;
-                else
-                    g[4 * j + c] = in ? ld_one(reinterpret_cast<const float *>(tr.g) + local + e0 + c) : 0.0f;
+            for (int k = 0; k < 4; ++k) {
+                const bool in = e0 + k < c.n;
+                r.p[4 * j + k] = in ? ld_one(c.p + e0 + k) : 0.0f;
+                if constexpr (kGradBf16) {
+                    const uint32_t h = in ? ld_one(reinterpret_cast<const uint16_t *>(c.g) + e0 + k) : 0u;
+                    if (k & 1) r.g[2 * j + k / 2] |= h << 16;
+                    else r.g[2 * j + k / 2] = h;
+                } else {
+                    r.g[4 * j + k] = in ? __float_as_uint(ld_one(reinterpret_cast<const float *>(c.g) + e0 + k)) : 0u;
+                }
             }
         }
-    }
-
-    // ---- load and decode the stored moments (padding entries hold zeros)
-    float Am = 0.0f, Av = 0.0f;
-    if constexpr (kQuantM) Am = a.m_scale[blk];
-    if constexpr (kQuantV) Av = a.v_scale[blk];
-    constexpr float Rm = 1.0f / 127.0f;
-    constexpr float Rv = 1.0f / 255.0f;
-#pragma unroll
-    for (int j = 0; j < kGroups; ++j) {
-        const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
-        const size_t s = d.gidx + e0;
-        const bool in = e0 < npad;
+        // state: padding entries of the segment hold zeros
+        const size_t s = c.gidx + e0;
+        const bool in = kFull || e0 < c.npad;
         if constexpr (kStore == kStoreBf16) {
             u32x2 hm = {0u, 0u}, hv = {0u, 0u};
             if (in) {
                 hm = ld_u32x2(reinterpret_cast<const uint16_t *>(a.m_state) + s);
                 hv = ld_u32x2(reinterpret_cast<const uint16_t *>(a.v_state) + s);
             }
-            mo[4 * j + 0] = bf16_to_f32(hm.x & 0xFFFFu); mo[4 * j + 1] = bf16_to_f32(hm.x >> 16);
-            mo[4 * j + 2] = bf16_to_f32(hm.y & 0xFFFFu); mo[4 * j + 3] = bf16_to_f32(hm.y >> 16);
-            vo[4 * j + 0] = bf16_to_f32(hv.x & 0xFFFFu); vo[4 * j + 1] = bf16_to_f32(hv.x >> 16);
-            vo[4 * j + 2] = bf16_to_f32(hv.y & 0xFFFFu); vo[4 * j + 3] = bf16_to_f32(hv.y >> 16);
+            r.m[2 * j] = hm.x; r.m[2 * j + 1] = hm.y;
+            r.v[2 * j] = hv.x; r.v[2 * j + 1] = hv.y;
         } else {
-            uint32_t cv = 0;
-            if (in) cv = ld_u32(reinterpret_cast<const uint8_t *>(a.v_state) + s);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) vo[4 * j + c] = ((float)((cv >> (8 * c)) & 0xFFu) * Rv) * Av;
-            if constexpr (kQuantM) {
-                uint32_t cm = 0;
-                if (in) cm = ld_u32(reinterpret_cast<const int8_t *>(a.m_state) + s);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int32_t q = ((int32_t)(cm << (24 - 8 * c))) >> 24;
-                    mo[4 * j + c] = ((float)q * Rm) * Am;
-                }
+            r.v[j] = in ? ld_u32(reinterpret_cast<const uint8_t *>(a.v_state) + s) : 0u;
+            if constexpr (kStore == kStoreQ8) {
+                r.m[j] = in ? ld_u32(reinterpret_cast<const int8_t *>(a.m_state) + s) : 0u;
             } else {
                 f32x4 mf = {0.f, 0.f, 0.f, 0.f};
                 if (in) mf = ld_f32x4(reinterpret_cast<const float *>(a.m_state) + s);
-                mo[4 * j + 0] = mf.x; mo[4 * j + 1] = mf.y; mo[4 * j + 2] = mf.z; mo[4 * j + 3] = mf.w;
+                r.m[4 * j + 0] = __float_as_uint(mf.x); r.m[4 * j + 1] = __float_as_uint(mf.y);
+                r.m[4 * j + 2] = __float_as_uint(mf.z); r.m[4 * j + 3] = __float_as_uint(mf.w);
+            }
+        }
+    }
+}
+
+// LDS of one block's max reduction.
+struct BlockLds {
+    float red[2][kWaves];
+};
+
+// LDS of the percentile statistic (radix-select histogram + scan scratch).
+template <bool kPct>
+struct SelectLds {
+    __device__ uint32_t *hist() { return nullptr; }
+    __device__ uint32_t *scratch() { return nullptr; }
+};
+template <>
+struct SelectLds<true> {
+    uint32_t h[kBlock];
+    uint32_t s[kWaves + 2];
+    __device__ uint32_t *hist() { return h; }
+    __device__ uint32_t *scratch() { return s; }
+};
+
+// Decode, update, store params; block statistic; requantize and store state.
+template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kFull>
+__device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx &c,
+                                              const BlockRegs<kStore, kGradBf16> &r, BlockLds &lds,
+                                              SelectLds<kPct> &sel) {
+    constexpr bool kQuantM = (kStore == kStoreQ8);
+    const int tid = threadIdx.x;
+    float p[kItems], g[kItems], mo[kItems], vo[kItems];
+
+    // ---- decode
+    constexpr float Rm = 1.0f / 127.0f;
+    constexpr float Rv = 1.0f / 255.0f;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        p[i] = r.p[i];
+        if constexpr (kGradBf16) g[i] = bf16_to_f32((r.g[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+        else g[i] = __uint_as_float(r.g[i]);
+        if constexpr (kStore == kStoreBf16) {
+            mo[i] = bf16_to_f32((r.m[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+            vo[i] = bf16_to_f32((r.v[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+        } else {
+            vo[i] = ((float)((r.v[i / 4] >> (8 * (i & 3))) & 0xFFu) * Rv) * r.Av;
+            if constexpr (kQuantM) {
+                const int32_t q = ((int32_t)(r.m[i / 4] << (24 - 8 * (i & 3)))) >> 24;
+                mo[i] = ((float)q * Rm) * r.Am;
+            } else {
+                mo[i] = __uint_as_float(r.m[i]);
             }
         }
     }
 
     // ---- the Adam/AdamW element update (moments stay in registers)
+    if (a.l2) {  // Adam with L2-coupled weight decay (uniform branch)
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) g[i] = fmaf(a.wd, p[i], g[i]);
+    }
     float mmax = 0.0f, vmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-        float gi = g[i];
-        if (a.l2) gi = fmaf(a.wd, p[i], gi);
+        const float gi = g[i];
         const float m = fmaf(a.beta1, mo[i], a.omb1 * gi);
         const float v = fmaf(a.beta2, vo[i], a.omb2 * (gi * gi));
         const float den = fmaf(sqrtf(v), a.ibc2, a.eps);
@@ -298,12 +412,12 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
         const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
-        if (e0 + 4 <= n) {
-            st_f32x4(pp + e0, f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]});
+        if (kFull || e0 + 4 <= c.n) {
+            st_f32x4(c.p + e0, f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]});
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (e0 + c < n) st_one(pp + e0 + c, p[4 * j + c]);
+            for (int k = 0; k < 4; ++k)
+                if (e0 + k < c.n) st_one(c.p + e0 + k, p[4 * j + k]);
         }
     }
 
@@ -311,8 +425,8 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
 #pragma unroll
         for (int j = 0; j < kGroups; ++j) {
             const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
-            if (e0 < npad) {
-                const size_t s = d.gidx + e0;
+            if (kFull || e0 < c.npad) {
+                const size_t s = c.gidx + e0;
                 const u32x2 hm = {f32_to_bf16(mo[4 * j]) | (f32_to_bf16(mo[4 * j + 1]) << 16),
                                   f32_to_bf16(mo[4 * j + 2]) | (f32_to_bf16(mo[4 * j + 3]) << 16)};
                 const u32x2 hv = {f32_to_bf16(vo[4 * j]) | (f32_to_bf16(vo[4 * j + 1]) << 16),
@@ -321,29 +435,25 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
                 st_u32x2(reinterpret_cast<uint16_t *>(a.v_state) + s, hv);
             }
         }
-        return;
     } else {
         // ---- block statistic
-        __shared__ float red[2][kWaves];
-        block_max2(mmax, vmax, red);
+        block_max2(mmax, vmax, lds.red);
         float Amn = mmax, Avn = vmax;
         if constexpr (kPct) {
-            __shared__ uint32_t hist[kBlock];
-            __shared__ uint32_t scratch[kWaves + 2];
-            const uint32_t rank = (uint32_t)floor(a.pfrac * (double)(n - 1)) + (kBlock - n);
+            const uint32_t rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
             uint32_t key[kItems];
             if constexpr (kQuantM) {
 #pragma unroll
                 for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(mo[i]) & 0x7FFFFFFFu;
-                const float sel = __uint_as_float(block_select(key, rank, hist, scratch));
-                Amn = sel < kTiny ? mmax : sel;
-                __syncthreads();  // hist/scratch reused below
+                const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
+                Amn = sv < kTiny ? mmax : sv;
             }
 #pragma unroll
             for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(vo[i]) & 0x7FFFFFFFu;
-            const float sel = __uint_as_float(block_select(key, rank, hist, scratch));
-            Avn = sel < kTiny ? vmax : sel;
+            const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
+            Avn = sv < kTiny ? vmax : sv;
         }
+        constexpr bool kClip = kSR || kPct;
         const bool mzero = !(Amn >= kTiny), vzero = !(Avn >= kTiny);
         const float rm = mzero ? 0.0f : 127.0f / Amn;
         const float rv = vzero ? 0.0f : 255.0f / Avn;
@@ -352,32 +462,32 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
 #pragma unroll
         for (int j = 0; j < kGroups; ++j) {
             const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
-            if (e0 >= npad) continue;
-            const size_t s = d.gidx + e0;
+            if (!kFull && e0 >= c.npad) continue;
+            const size_t s = c.gidx + e0;
             uint32_t w[4] = {0u, 0u, 0u, 0u};
             if constexpr (kSR) {
                 const uint64_t grp = s >> 2;
-                uint32_t c[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), a.t_lo, a.t_hi};
-                philox4x32_10(c, a.seed_lo, a.seed_hi);
-                w[0] = c[0]; w[1] = c[1]; w[2] = c[2]; w[3] = c[3];
+                uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), a.t_lo, a.t_hi};
+                philox4x32_10(ctr, a.seed_lo, a.seed_hi);
+                w[0] = ctr[0]; w[1] = ctr[1]; w[2] = ctr[2]; w[3] = ctr[3];
             }
             uint32_t cv = 0;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float k = vzero ? 0.0f
-                                      : code_magnitude<kSR>(fabsf(vo[4 * j + c]), Avn, rv, 255.0f, w[c] >> 16);
-                cv |= ((uint32_t)k) << (8 * c);
+            for (int k = 0; k < 4; ++k) {
+                const float q = vzero ? 0.0f
+                                      : code_magnitude<kSR, kClip>(fabsf(vo[4 * j + k]), Avn, rv, 255.0f, w[k] >> 16);
+                cv |= ((uint32_t)q) << (8 * k);
             }
             st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s, cv);
             if constexpr (kQuantM) {
                 uint32_t cm = 0;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float x = mo[4 * j + c];
-                    const float k = mzero ? 0.0f
-                                          : code_magnitude<kSR>(fabsf(x), Amn, rm, 127.0f, w[c] & 0xFFFFu);
-                    const int32_t q = x < 0.0f ? -(int32_t)k : (int32_t)k;
-                    cm |= ((uint32_t)q & 0xFFu) << (8 * c);
+                for (int k = 0; k < 4; ++k) {
+                    const float x = mo[4 * j + k];
+                    const float q = mzero ? 0.0f
+                                          : code_magnitude<kSR, kClip>(fabsf(x), Amn, rm, 127.0f, w[k] & 0xFFFFu);
+                    const int32_t qs = (int32_t)copysignf(q, x);  // -0 converts to 0
+                    cm |= ((uint32_t)qs & 0xFFu) << (8 * k);
                 }
                 st_u32(reinterpret_cast<int8_t *>(a.m_state) + s, cm);
             } else {
@@ -386,41 +496,84 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
             }
         }
         if (tid == 0) {
-            if constexpr (kQuantM) a.m_scale[blk] = mzero ? 0.0f : Amn;
-            a.v_scale[blk] = vzero ? 0.0f : Avn;
+            if constexpr (kQuantM) a.m_scale[c.slot] = mzero ? 0.0f : Amn;
+            a.v_scale[c.slot] = vzero ? 0.0f : Avn;
         }
     }
 }
 
+// ---------------------------------------------------------------- kernel
+// One workgroup per block; workgroups beyond the grid limit loop (stride =
+// grid size).  Descriptors [0, n_full) are full blocks, whose path has no
+// tail checks; the rest are the tensors' ragged last blocks.
 template <int kStore, bool kGradBf16, bool kSR, bool kPct>
-hipError_t launch_one(const StepArgs &a, uint32_t nblk, hipStream_t stream) {
-    hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct>), dim3(nblk), dim3(kThreads), 0,
+__global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
+    __shared__ BlockLds lds;
+    __shared__ SelectLds<kPct> sel;
+    for (uint32_t i = blockIdx.x; i < a.n_all; i += gridDim.x) {
+        BlockRegs<kStore, kGradBf16> r;
+        const BlockCtx c = load_ctx<kGradBf16>(a, i);
+        if (i < a.n_full) {
+            load_data<kStore, kGradBf16, true>(a, c, r);
+            process_block<kStore, kGradBf16, kSR, kPct, true>(a, c, r, lds, sel);
+        } else {
+            load_data<kStore, kGradBf16, false>(a, c, r);
+            process_block<kStore, kGradBf16, kSR, kPct, false>(a, c, r, lds, sel);
+        }
+        if (i + gridDim.x < a.n_all) __syncthreads();  // LDS reused by the next block
+    }
+}
+
+// Occupancy cap.  Too many outstanding requests thrash the HBM pages: with
+// bf16 moments (no block statistic, short compute) the step streams fastest
+// with at most 3 workgroups resident per CU, so that launch reserves LDS it
+// does not use (CU LDS is 160 KiB).  The 8-bit variants spend longer per
+// block (statistic, requantization) and need every resident workgroup to
+// keep enough bytes in flight, so they are not capped.
+constexpr int kCuLdsBytes = 160 * 1024;
+#ifndef ADAM_BF16_RESIDENT_PER_CU
+#define ADAM_BF16_RESIDENT_PER_CU 3
+#endif
+#ifndef ADAM_Q8_RESIDENT_PER_CU
+#define ADAM_Q8_RESIDENT_PER_CU 8
+#endif
+constexpr size_t reserve_lds(int resident) { return resident >= 8 ? 0 : kCuLdsBytes / (resident + 1) + 1024; }
+constexpr uint32_t kMaxGrid = (1u << 24) - 1;  // grid.x * 256 work-items < 2^32
+
+template <int kStore, bool kGradBf16, bool kSR, bool kPct>
+hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
+    const uint32_t grid = std::min<uint32_t>(a.n_all, kMaxGrid);
+    if (grid == 0) return hipSuccess;
+    constexpr int kResident = kStore == kStoreBf16 ? ADAM_BF16_RESIDENT_PER_CU : ADAM_Q8_RESIDENT_PER_CU;
+    constexpr size_t kStatic = sizeof(BlockLds) + sizeof(SelectLds<kPct>);
+    constexpr size_t kDyn = reserve_lds(kResident) > kStatic ? reserve_lds(kResident) - kStatic : 0;
+    hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct>), dim3(grid), dim3(kThreads), kDyn,
                        stream, a);
     return hipGetLastError();
 }
 
 template <int kStore, bool kGradBf16>
-hipError_t launch_q(const Variant &v, const StepArgs &a, uint32_t nblk, hipStream_t stream) {
+hipError_t launch_q(const Variant &v, const StepArgs &a, hipStream_t stream) {
     if (v.stochastic)
-        return v.percentile ? launch_one<kStore, kGradBf16, true, true>(a, nblk, stream)
-                            : launch_one<kStore, kGradBf16, true, false>(a, nblk, stream);
-    return v.percentile ? launch_one<kStore, kGradBf16, false, true>(a, nblk, stream)
-                        : launch_one<kStore, kGradBf16, false, false>(a, nblk, stream);
+        return v.percentile ? launch_one<kStore, kGradBf16, true, true>(a, stream)
+                            : launch_one<kStore, kGradBf16, true, false>(a, stream);
+    return v.percentile ? launch_one<kStore, kGradBf16, false, true>(a, stream)
+                        : launch_one<kStore, kGradBf16, false, false>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_step(const Variant &v, const StepArgs &a, uint32_t nblk, hipStream_t stream) {
+hipError_t launch_step(const Variant &v, const StepArgs &a, hipStream_t stream) {
     switch (v.storage) {
     case kStoreBf16:
-        return v.grad_bf16 ? launch_one<kStoreBf16, true, false, false>(a, nblk, stream)
-                           : launch_one<kStoreBf16, false, false, false>(a, nblk, stream);
+        return v.grad_bf16 ? launch_one<kStoreBf16, true, false, false>(a, stream)
+                           : launch_one<kStoreBf16, false, false, false>(a, stream);
     case kStoreQ8:
-        return v.grad_bf16 ? launch_q<kStoreQ8, true>(v, a, nblk, stream)
-                           : launch_q<kStoreQ8, false>(v, a, nblk, stream);
+        return v.grad_bf16 ? launch_q<kStoreQ8, true>(v, a, stream)
+                           : launch_q<kStoreQ8, false>(v, a, stream);
     case kStoreQ8VOnly:
-        return v.grad_bf16 ? launch_q<kStoreQ8VOnly, true>(v, a, nblk, stream)
-                           : launch_q<kStoreQ8VOnly, false>(v, a, nblk, stream);
+        return v.grad_bf16 ? launch_q<kStoreQ8VOnly, true>(v, a, stream)
+                           : launch_q<kStoreQ8VOnly, false>(v, a, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -18,6 +18,18 @@
 
 using namespace adam_mi355x;
 
+namespace {
+constexpr int kTableSlots = 4;  // resident pointer tables per state
+constexpr int kStageSlots = 8;  // pinned staging buffers per state
+
+struct TableSlot {
+    TensorRef *dev = nullptr;
+    std::vector<TensorRef> ptrs;  // the pointer set this table holds
+    uint64_t last_use = 0;
+    bool valid = false;
+};
+}  // namespace
+
 struct adam_state {
     int device = -1;
     adam_layout layout{};
@@ -25,12 +37,19 @@ struct adam_state {
     std::vector<int64_t> numels;
     int64_t padded = 0;   // sum of pad16(numel)
     int64_t nblocks = 0;
+    int64_t n_full = 0;   // blocks of 2048 elements (listed first)
     BlockDesc *d_desc = nullptr;
-    TensorRef *d_tensors = nullptr;
-    TensorRef *h_tensors = nullptr;      // pinned staging for the pointer table
-    std::vector<TensorRef> last;         // pointers the device table holds
-    bool table_valid = false;
-    hipEvent_t upload_done = nullptr;    // staging buffer reusable once this fires
+    // Device copies of the caller's per-tensor {param, grad} pointer pairs.
+    // A few recently used pointer sets stay resident, so a caller that
+    // alternates between gradient buffers uploads nothing; a new set is
+    // staged through a ring of pinned buffers so the host does not wait for
+    // earlier uploads unless the ring wraps onto one still queued.
+    TableSlot tables[kTableSlots];
+    uint64_t table_clock = 0;
+    TensorRef *stage[kStageSlots] = {};
+    hipEvent_t stage_done[kStageSlots] = {};
+    bool stage_pending[kStageSlots] = {};
+    int next_stage = 0;
     void *m = nullptr;                   // bf16 / int8 / fp32 first moment
     void *v = nullptr;                   // bf16 / uint8 second moment
     float *m_scale = nullptr;
@@ -112,10 +131,12 @@ void release(adam_state *s) {
         (void)hipGetDevice(&cur);
         if (cur != s->device) (void)hipSetDevice(s->device);
         (void)hipDeviceSynchronize();
-        if (s->upload_done) (void)hipEventDestroy(s->upload_done);
+        for (int i = 0; i < kStageSlots; ++i) {
+            if (s->stage_done[i]) (void)hipEventDestroy(s->stage_done[i]);
+            (void)hipHostFree(s->stage[i]);
+        }
+        for (int i = 0; i < kTableSlots; ++i) (void)hipFree(s->tables[i].dev);
         (void)hipFree(s->d_desc);
-        (void)hipFree(s->d_tensors);
-        (void)hipHostFree(s->h_tensors);
         (void)hipFree(s->m);
         (void)hipFree(s->v);
         (void)hipFree(s->m_scale);
@@ -195,22 +216,27 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
     s->layout = *layout;
     s->n_tensors = n_tensors;
     s->numels.assign(numels, numels + n_tensors);
-    std::vector<BlockDesc> desc;
+    // descriptors: full blocks first, then each tensor's ragged last block;
+    // scale slots keep the tensor-major block numbering
+    std::vector<BlockDesc> desc, tails;
+    int64_t slot = 0;
     for (int32_t k = 0; k < n_tensors; ++k) {
         const int64_t n = numels[k];
-        for (int64_t b = 0; b * kBlock < n; ++b) {
+        for (int64_t b = 0; b * kBlock < n; ++b, ++slot) {
             const int64_t len = std::min<int64_t>(kBlock, n - b * kBlock);
-            desc.push_back(BlockDesc{(uint64_t)(s->padded + b * kBlock), (uint32_t)k,
-                                     (uint32_t)((b << kBlockBits) | (len - 1))});
+            const BlockDesc d{(uint32_t)((s->padded + b * kBlock) / 16), (uint32_t)k,
+                              (uint32_t)((b << kBlockBits) | (len - 1)), (uint32_t)slot};
+            (len == kBlock ? desc : tails).push_back(d);
         }
         s->padded += pad16(n);
     }
+    s->n_full = (int64_t)desc.size();
+    desc.insert(desc.end(), tails.begin(), tails.end());
     s->nblocks = (int64_t)desc.size();
-    if (s->nblocks >= (int64_t(1) << 32)) {
+    if (s->nblocks >= (int64_t(1) << 32) || s->padded / 16 >= (int64_t(1) << 32)) {
         release(s);
-        return fail(ADAM_EINVAL, "more than 2^32 - 1 blocks");
+        return fail(ADAM_EINVAL, "state too large: more than 2^32 - 1 blocks or 2^36 elements");
     }
-    s->last.assign(n_tensors, TensorRef{nullptr, nullptr});
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
     int64_t per_elem, per_block;
@@ -243,17 +269,25 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
         }
     }
     if (n_tensors > 0) {
-        if (hipMalloc((void **)&s->d_tensors, n_tensors * sizeof(TensorRef)) != hipSuccess ||
-            hipHostMalloc((void **)&s->h_tensors, n_tensors * sizeof(TensorRef), hipHostMallocDefault) !=
-                hipSuccess) {
-            (void)hipGetLastError();
-            release(s);
-            return fail(ADAM_ENOMEM, "pointer table allocation failed");
+        const size_t tbytes = (size_t)n_tensors * sizeof(TensorRef);
+        for (int i = 0; i < kTableSlots; ++i) {
+            if (hipMalloc((void **)&s->tables[i].dev, tbytes) != hipSuccess) {
+                (void)hipGetLastError();
+                release(s);
+                return fail(ADAM_ENOMEM, "pointer table allocation failed");
+            }
         }
-    }
-    if ((e = hipEventCreateWithFlags(&s->upload_done, hipEventDisableTiming)) != hipSuccess) {
-        release(s);
-        return hip_fail(e, "hipEventCreate");
+        for (int i = 0; i < kStageSlots; ++i) {
+            if (hipHostMalloc((void **)&s->stage[i], tbytes, hipHostMallocDefault) != hipSuccess) {
+                (void)hipGetLastError();
+                release(s);
+                return fail(ADAM_ENOMEM, "pinned staging allocation failed");
+            }
+            if ((e = hipEventCreateWithFlags(&s->stage_done[i], hipEventDisableTiming)) != hipSuccess) {
+                release(s);
+                return hip_fail(e, "hipEventCreate");
+            }
+        }
     }
     if ((e = hipStreamSynchronize(stream)) != hipSuccess) {
         release(s);
@@ -320,23 +354,40 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
                                      std::to_string(dev));
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
 
-    // refresh the device pointer table when the caller's pointers changed
-    bool changed = !s->table_valid;
-    for (int32_t k = 0; k < s->n_tensors && !changed; ++k)
-        changed = s->last[k].p != params[k] || s->last[k].g != grads[k];
-    if (changed) {
-        if ((e = hipEventSynchronize(s->upload_done)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-        for (int32_t k = 0; k < s->n_tensors; ++k) s->last[k] = TensorRef{params[k], grads[k]};
-        std::memcpy(s->h_tensors, s->last.data(), s->n_tensors * sizeof(TensorRef));
-        e = hipMemcpyAsync(s->d_tensors, s->h_tensors, s->n_tensors * sizeof(TensorRef), hipMemcpyHostToDevice,
-                           stream);
-        if (e != hipSuccess) {
-            s->table_valid = false;
-            return hip_fail(e, "pointer table upload");
-        }
-        if ((e = hipEventRecord(s->upload_done, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        s->table_valid = true;
+    // the device pointer table holding these pointers (uploading it if new)
+    int slot = -1;
+    for (int i = 0; i < kTableSlots && slot < 0; ++i) {
+        const TableSlot &ts = s->tables[i];
+        if (!ts.valid) continue;
+        bool same = true;
+        for (int32_t k = 0; k < s->n_tensors && same; ++k)
+            same = ts.ptrs[k].p == params[k] && ts.ptrs[k].g == grads[k];
+        if (same) slot = i;
     }
+    if (slot < 0) {
+        slot = 0;  // least recently used (or never used) table
+        for (int i = 1; i < kTableSlots; ++i)
+            if (!s->tables[i].valid || (s->tables[slot].valid && s->tables[i].last_use < s->tables[slot].last_use))
+                slot = i;
+        TableSlot &ts = s->tables[slot];
+        const int st = s->next_stage;
+        s->next_stage = (st + 1) % kStageSlots;
+        if (s->stage_pending[st]) {  // the ring wrapped onto a copy still queued
+            if ((e = hipEventSynchronize(s->stage_done[st])) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+            s->stage_pending[st] = false;
+        }
+        ts.valid = false;
+        ts.ptrs.resize(s->n_tensors);
+        for (int32_t k = 0; k < s->n_tensors; ++k) ts.ptrs[k] = TensorRef{params[k], grads[k]};
+        std::memcpy(s->stage[st], ts.ptrs.data(), s->n_tensors * sizeof(TensorRef));
+        // stream order puts this copy after every earlier kernel that reads ts.dev
+        e = hipMemcpyAsync(ts.dev, s->stage[st], s->n_tensors * sizeof(TensorRef), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "pointer table upload");
+        if ((e = hipEventRecord(s->stage_done[st], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        s->stage_pending[st] = true;
+        ts.valid = true;
+    }
+    s->tables[slot].last_use = ++s->table_clock;
 
     // host scalars: fp64, each rounded once to fp32
     const double b1 = hp->beta1, b2 = hp->beta2;
@@ -345,7 +396,7 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
     const bool decoupled = (hp->flags & ADAM_F_DECOUPLED_WD) != 0;
     StepArgs a{};
     a.desc = s->d_desc;
-    a.tensors = s->d_tensors;
+    a.tensors = s->tables[slot].dev;
     a.m_state = s->m;
     a.v_state = s->v;
     a.m_scale = s->m_scale;
@@ -366,15 +417,11 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
     a.t_lo = (uint32_t)(uint64_t)hp->t;
     a.t_hi = (uint32_t)((uint64_t)hp->t >> 32);
 
+    a.n_full = (uint32_t)s->n_full;
+    a.n_all = (uint32_t)s->nblocks;
     Variant v{s->layout.storage, s->layout.grad_dtype == ADAM_GRAD_BF16, (hp->flags & ADAM_F_STOCHASTIC) != 0,
               (hp->flags & ADAM_F_PERCENTILE) != 0};
-    // grid.x * 256 work-items must stay below 2^32: launch in chunks
-    const int64_t kMaxBlocksPerLaunch = int64_t(1) << 23;
-    for (int64_t b0 = 0; b0 < s->nblocks; b0 += kMaxBlocksPerLaunch) {
-        a.blk0 = (uint32_t)b0;
-        const uint32_t nb = (uint32_t)std::min<int64_t>(kMaxBlocksPerLaunch, s->nblocks - b0);
-        if ((e = launch_step(v, a, nb, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
-    }
+    if ((e = launch_step(v, a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
     return ADAM_OK;
 }
 

@@ -331,3 +331,31 @@ def test_error_paths_enqueue_nothing():
     assert torch.equal(p, before)
     st.destroy()
     bst.destroy()
+
+
+def test_alternating_gradient_buffers_beyond_the_table_cache():
+    # six gradient buffer sets in rotation (more than the resident pointer
+    # tables), params moved twice: every step must still read the right tensors
+    numels = [3000, 2048, 77]
+    params = workloads.host_params(27, numels)
+    dev_p = [torch.from_numpy(x.copy()).cuda() for x in params]
+    bufs = [[torch.empty(n, device="cuda") for n in numels] for _ in range(6)]
+    st = ma.adam_state_create(numels, "q8")
+    ost = oracle.OracleState(numels, "q8")
+    stats = Stats()
+    order = [0, 1, 2, 3, 4, 5, 0, 2, 4, 1, 3, 5, 5, 0]
+    for t, b in enumerate(order, start=1):
+        grads = workloads.host_grads(27, numels, t)
+        for k in range(len(numels)):
+            bufs[b][k].copy_(torch.from_numpy(grads[k]))
+        if t in (5, 11):
+            dev_p = [x.clone() for x in dev_p]
+        ma.adam_step(st, dev_p, bufs[b], t=t, stochastic=True, seed=5, **HP)
+        ost.step(params, grads, t=t, stochastic=True, seed=5, **HP)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, True, stats, f"t={t}")
+    st.destroy()
