@@ -176,6 +176,44 @@ int adam_state_read(adam_state *s, int32_t which, void *dst, int64_t nbytes, voi
 int adam_state_write(adam_state *s, int32_t which, const void *src, int64_t nbytes,
                      void *hip_stream);
 
+/*
+ * Checkpoint / resume of the whole optimizer state: the 8-bit Adam page
+ * lists full serialization support, and its follow-up fix writes a presence
+ * marker per moment so that a reader never assumes a buffer the writer did
+ * not store.  The serialized form is a self-describing little-endian byte
+ * stream in host memory:
+ *   header   "MEAMSTAT", u32 version (1), u32 header bytes (32 + 8*n),
+ *            i32 storage, i32 grad_dtype, i32 block_size, i32 n_tensors,
+ *            i64 numels[n_tensors]
+ *   records  one per state buffer the storage mode has (enum adam_buffer
+ *            order): u32 buffer id, u32 0, u64 byte count, the bytes, zero
+ *            padding to a multiple of 8
+ *   trailer  u32 0xFFFFFFFF, u32 record count, u64 checksum (a 64-bit
+ *            multiply-xor hash over every preceding byte, 8 bytes at a time)
+ * adam_state_serialized_bytes: the stream's size for this state (< 0 on a
+ * NULL state).
+ * adam_state_save: writes the stream to dst (host memory, nbytes exactly
+ * the serialized size); the device copies are ordered on hip_stream after
+ * earlier work on the state, and the call returns once dst is complete.
+ * adam_state_load: validates the whole stream on the host (magic, version,
+ * layout, numels, the exact set and sizes of the records, trailer and
+ * checksum) before any device call, then creates a state on the current
+ * device holding exactly the saved contents (free with adam_state_destroy).
+ * A resumed run is bit-identical to an uninterrupted one.
+ * Errors: EINVAL (NULL pointers, size mismatch, any validation failure),
+ * ENOMEM, EDEVICE.
+ */
+int64_t adam_state_serialized_bytes(const adam_state *s);
+int adam_state_save(adam_state *s, void *dst, int64_t nbytes, void *hip_stream);
+int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip_stream);
+
+/* Describes a state (pure host): its layout and tensor count, and the
+   first min(n_tensors, max_tensors) element counts into numels (which may
+   be NULL when max_tensors is 0).  Returns the tensor count, or < 0 on a
+   NULL state or layout pointer. */
+int32_t adam_state_describe(const adam_state *s, adam_layout *layout, int64_t *numels,
+                            int32_t max_tensors);
+
 /* Frees every buffer of the state (after synchronizing the device).
    NULL is ignored. */
 void adam_state_destroy(adam_state *s);

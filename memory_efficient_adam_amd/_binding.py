@@ -65,6 +65,14 @@ def library():
     L.adam_state_read.restype = ctypes.c_int
     L.adam_state_write.argtypes = [vp, ctypes.c_int32, vp, ctypes.c_int64, vp]
     L.adam_state_write.restype = ctypes.c_int
+    L.adam_state_describe.argtypes = [vp, ctypes.POINTER(adam_layout), i64p, ctypes.c_int32]
+    L.adam_state_describe.restype = ctypes.c_int32
+    L.adam_state_serialized_bytes.argtypes = [vp]
+    L.adam_state_serialized_bytes.restype = ctypes.c_int64
+    L.adam_state_save.argtypes = [vp, vp, ctypes.c_int64, vp]
+    L.adam_state_save.restype = ctypes.c_int
+    L.adam_state_load.argtypes = [ctypes.POINTER(vp), vp, ctypes.c_int64, vp]
+    L.adam_state_load.restype = ctypes.c_int
     L.adam_state_destroy.argtypes = [vp]
     L.adam_state_destroy.restype = None
     L.adam_last_error.argtypes = []
@@ -199,3 +207,42 @@ def adam_state_write(state, which, src, stream=None):
         raise ValueError("size mismatch")
     _check(library().adam_state_write(state.handle, BUFFERS[which], src.data_ptr(), nbytes,
                                       _stream(stream)))
+
+
+def adam_state_describe(state):
+    """(layout, numels) of a state, as the library holds them."""
+    lay = adam_layout()
+    n = library().adam_state_describe(state.handle, ctypes.byref(lay), None, 0)
+    if n < 0:
+        raise AdamError(int(n), adam_last_error())
+    arr = (ctypes.c_int64 * max(n, 1))()
+    library().adam_state_describe(state.handle, ctypes.byref(lay), arr, n)
+    return lay, [int(arr[i]) for i in range(n)]
+
+
+def adam_state_serialized_bytes(state):
+    n = library().adam_state_serialized_bytes(state.handle)
+    if n < 0:
+        raise AdamError(int(n), adam_last_error())
+    return int(n)
+
+
+def adam_state_save(state, stream=None):
+    """The serialized state as a numpy uint8 array (host memory)."""
+    import numpy as np
+    out = np.empty(adam_state_serialized_bytes(state), np.uint8)
+    _check(library().adam_state_save(state.handle, out.ctypes.data, out.size, _stream(stream)))
+    return out
+
+
+def adam_state_load(buf, stream=None):
+    """A new state holding the contents of a serialized state (bytes-like or
+    numpy uint8 array)."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.frombuffer(buf, np.uint8) if not isinstance(buf, np.ndarray)
+                               else buf.view(np.uint8))
+    h = ctypes.c_void_p()
+    _check(library().adam_state_load(ctypes.byref(h), arr.ctypes.data, arr.size, _stream(stream)))
+    st = AdamState(h.value, [], adam_layout())
+    st.layout, st.numels = adam_state_describe(st)
+    return st

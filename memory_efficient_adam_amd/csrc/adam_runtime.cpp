@@ -299,6 +299,192 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
 
 void adam_state_destroy(adam_state *s) { release(s); }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- checkpoint
+namespace {
+constexpr char kMagic[8] = {'M', 'E', 'A', 'M', 'S', 'T', 'A', 'T'};
+constexpr uint32_t kFormatVersion = 1;
+constexpr uint32_t kEndMarker = 0xFFFFFFFFu;
+
+int64_t align8(int64_t n) { return (n + 7) / 8 * 8; }
+
+// 64-bit multiply-xor hash over whole 8-byte words (little-endian), then the
+// remaining bytes one at a time.
+uint64_t stream_hash(const uint8_t *p, int64_t n) {
+    uint64_t h = 0x9E3779B97F4A7C15ull ^ (uint64_t)n;
+    int64_t i = 0;
+    for (; i + 8 <= n; i += 8) {
+        uint64_t w;
+        std::memcpy(&w, p + i, 8);
+        h = (h ^ w) * 0x100000001B3ull;
+        h ^= h >> 29;
+    }
+    for (; i < n; ++i) h = (h ^ p[i]) * 0x100000001B3ull;
+    return h ^ (h >> 32);
+}
+
+// The state buffers a storage mode has, in enum adam_buffer order.
+std::vector<int32_t> buffers_of(int32_t storage) {
+    switch (storage) {
+    case ADAM_STORE_BF16: return {ADAM_BUF_M_BF16, ADAM_BUF_V_BF16};
+    case ADAM_STORE_Q8: return {ADAM_BUF_M_CODES, ADAM_BUF_V_CODES, ADAM_BUF_M_SCALE, ADAM_BUF_V_SCALE};
+    default: return {ADAM_BUF_V_CODES, ADAM_BUF_V_SCALE, ADAM_BUF_M_F32};
+    }
+}
+
+int64_t header_bytes(int32_t n_tensors) { return 32 + 8 * (int64_t)n_tensors; }
+
+template <class T>
+void put(uint8_t *base, int64_t &off, T v) {
+    std::memcpy(base + off, &v, sizeof(T));
+    off += sizeof(T);
+}
+template <class T>
+bool get(const uint8_t *base, int64_t n, int64_t &off, T &v) {
+    if (off + (int64_t)sizeof(T) > n) return false;
+    std::memcpy(&v, base + off, sizeof(T));
+    off += sizeof(T);
+    return true;
+}
+}  // namespace
+
+extern "C" {
+
+int64_t adam_state_serialized_bytes(const adam_state *s) {
+    if (!s) return fail(ADAM_EINVAL, "state is NULL");
+    int64_t n = header_bytes(s->n_tensors);
+    for (int32_t b : buffers_of(s->layout.storage)) n += 16 + align8(buffer_of(s, b).bytes);
+    return n + 16;
+}
+
+int adam_state_save(adam_state *s, void *dst, int64_t nbytes, void *hip_stream) {
+    if (!s || !dst) return fail(ADAM_EINVAL, "state or destination is NULL");
+    const int64_t need = adam_state_serialized_bytes(s);
+    if (nbytes != need)
+        return fail(ADAM_EINVAL, "nbytes " + std::to_string(nbytes) + " != serialized size " + std::to_string(need));
+    uint8_t *out = static_cast<uint8_t *>(dst);
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    int64_t off = 0;
+    std::memcpy(out, kMagic, 8);
+    off = 8;
+    put<uint32_t>(out, off, kFormatVersion);
+    put<uint32_t>(out, off, (uint32_t)header_bytes(s->n_tensors));
+    put<int32_t>(out, off, s->layout.storage);
+    put<int32_t>(out, off, s->layout.grad_dtype);
+    put<int32_t>(out, off, s->layout.block_size);
+    put<int32_t>(out, off, s->n_tensors);
+    for (int32_t k = 0; k < s->n_tensors; ++k) put<int64_t>(out, off, s->numels[k]);
+    const std::vector<int32_t> bufs = buffers_of(s->layout.storage);
+    hipError_t e;
+    for (int32_t b : bufs) {
+        const BufferView v = buffer_of(s, b);
+        put<uint32_t>(out, off, (uint32_t)b);
+        put<uint32_t>(out, off, 0u);
+        put<uint64_t>(out, off, (uint64_t)v.bytes);
+        if (v.bytes > 0 &&
+            (e = hipMemcpyAsync(out + off, v.ptr, (size_t)v.bytes, hipMemcpyDeviceToHost, stream)) != hipSuccess)
+            return hip_fail(e, "state copy to host");
+        std::memset(out + off + v.bytes, 0, (size_t)(align8(v.bytes) - v.bytes));
+        off += align8(v.bytes);
+    }
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    put<uint32_t>(out, off, kEndMarker);
+    put<uint32_t>(out, off, (uint32_t)bufs.size());
+    const uint64_t h = stream_hash(out, off);
+    put<uint64_t>(out, off, h);
+    return ADAM_OK;
+}
+
+int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip_stream) {
+    if (!out || !src) return fail(ADAM_EINVAL, "out or source is NULL");
+    *out = nullptr;
+    const uint8_t *in = static_cast<const uint8_t *>(src);
+    int64_t off = 0;
+    if (nbytes < 32 + 16 || std::memcmp(in, kMagic, 8) != 0) return fail(ADAM_EINVAL, "not a serialized Adam state");
+    off = 8;
+    uint32_t version = 0, hbytes = 0;
+    adam_layout lay{};
+    int32_t n_tensors = 0;
+    get(in, nbytes, off, version);
+    get(in, nbytes, off, hbytes);
+    get(in, nbytes, off, lay.storage);
+    get(in, nbytes, off, lay.grad_dtype);
+    get(in, nbytes, off, lay.block_size);
+    get(in, nbytes, off, n_tensors);
+    if (version != kFormatVersion) return fail(ADAM_EINVAL, "unsupported state format version " + std::to_string(version));
+    if (n_tensors < 0 || (int64_t)hbytes != header_bytes(n_tensors) || (int64_t)hbytes > nbytes - 16)
+        return fail(ADAM_EINVAL, "corrupt state header");
+    int rc = check_layout(&lay);
+    if (rc) return rc;
+    std::vector<int64_t> numels(n_tensors);
+    for (int32_t k = 0; k < n_tensors; ++k) get(in, nbytes, off, numels[k]);
+    if ((rc = check_numels(n_tensors, numels.data()))) return rc;
+    // the trailer and checksum cover everything before the checksum itself
+    if (nbytes % 8 != 0) return fail(ADAM_EINVAL, "serialized state size is not a multiple of 8");
+    uint64_t want_hash = 0;
+    std::memcpy(&want_hash, in + nbytes - 8, 8);
+    if (stream_hash(in, nbytes - 8) != want_hash) return fail(ADAM_EINVAL, "serialized state checksum mismatch");
+    // records: exactly the storage mode's buffers, in order, with the sizes this layout implies
+    const std::vector<int32_t> bufs = buffers_of(lay.storage);
+    int64_t padded = 0, nblocks = 0;
+    for (int64_t n : numels) {
+        padded += pad16(n);
+        nblocks += blocks_of(n);
+    }
+    std::vector<std::pair<int64_t, int64_t>> payload;  // (offset, bytes) per record
+    for (int32_t b : bufs) {
+        uint32_t id = 0, zero = 1;
+        uint64_t len = 0;
+        if (!get(in, nbytes, off, id) || !get(in, nbytes, off, zero) || !get(in, nbytes, off, len))
+            return fail(ADAM_EINVAL, "truncated serialized state");
+        int64_t expect = 0;
+        switch (b) {
+        case ADAM_BUF_M_CODES: case ADAM_BUF_V_CODES: expect = padded; break;
+        case ADAM_BUF_M_SCALE: case ADAM_BUF_V_SCALE: expect = 4 * nblocks; break;
+        case ADAM_BUF_M_BF16: case ADAM_BUF_V_BF16: expect = 2 * padded; break;
+        default: expect = 4 * padded; break;
+        }
+        if ((int32_t)id != b || zero != 0 || (int64_t)len != expect)
+            return fail(ADAM_EINVAL, "state record " + std::to_string(b) + " missing, out of order or of the wrong size");
+        if (off + align8((int64_t)len) > nbytes - 16) return fail(ADAM_EINVAL, "truncated serialized state");
+        payload.emplace_back(off, (int64_t)len);
+        off += align8((int64_t)len);
+    }
+    uint32_t end = 0, count = 0;
+    get(in, nbytes, off, end);
+    get(in, nbytes, off, count);
+    if (end != kEndMarker || count != bufs.size() || off != nbytes - 8)
+        return fail(ADAM_EINVAL, "corrupt serialized state trailer");
+
+    adam_state *s = nullptr;
+    if ((rc = adam_state_create(&s, n_tensors, numels.data(), &lay, hip_stream))) return rc;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t e;
+    for (size_t i = 0; i < bufs.size(); ++i) {
+        const BufferView v = buffer_of(s, bufs[i]);
+        if (v.bytes > 0 && (e = hipMemcpyAsync(v.ptr, in + payload[i].first, (size_t)v.bytes,
+                                               hipMemcpyHostToDevice, stream)) != hipSuccess) {
+            release(s);
+            return hip_fail(e, "state copy to device");
+        }
+    }
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) {
+        release(s);
+        return hip_fail(e, "hipStreamSynchronize");
+    }
+    *out = s;
+    return ADAM_OK;
+}
+
+int32_t adam_state_describe(const adam_state *s, adam_layout *layout, int64_t *numels, int32_t max_tensors) {
+    if (!s || !layout) return fail(ADAM_EINVAL, "state or layout is NULL");
+    if (max_tensors > 0 && !numels) return fail(ADAM_EINVAL, "numels is NULL");
+    *layout = s->layout;
+    for (int32_t k = 0; k < s->n_tensors && k < max_tensors; ++k) numels[k] = s->numels[k];
+    return s->n_tensors;
+}
+
 int64_t adam_state_buffer_bytes(const adam_state *s, int32_t which) {
     if (!s) return fail(ADAM_EINVAL, "state is NULL");
     const BufferView b = buffer_of(s, which);

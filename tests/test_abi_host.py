@@ -109,3 +109,92 @@ def test_step_and_buffer_calls_reject_null_state():
     assert lib.adam_state_write(None, 0, None, 0, None) == -1
     lib.adam_state_destroy(None)
     assert "NULL" in ma.adam_last_error()
+
+
+# ---------------------------------------------------------------- checkpoint stream
+def _stream_hash(b):
+    # the stream's 64-bit multiply-xor checksum (format definition in the header)
+    n = len(b)
+    h = (0x9E3779B97F4A7C15 ^ n) & 0xFFFFFFFFFFFFFFFF
+    i = 0
+    while i + 8 <= n:
+        w = int.from_bytes(b[i:i + 8], "little")
+        h = ((h ^ w) * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+        h ^= h >> 29
+        i += 8
+    while i < n:
+        h = ((h ^ b[i]) * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+        i += 1
+    return h ^ (h >> 32)
+
+
+def _serialized(numels, storage=2, records=None, version=1):
+    import struct
+    pad16 = [(n + 15) // 16 * 16 for n in numels]
+    blocks = sum(-(-n // 2048) for n in numels)
+    out = bytearray(b"MEAMSTAT")
+    out += struct.pack("<IIiiii", version, 32 + 8 * len(numels), storage, 0, 2048, len(numels))
+    out += struct.pack(f"<{len(numels)}q", *numels)
+    if records is None:
+        P = sum(pad16)
+        records = {2: [(0, P), (1, P), (2, 4 * blocks), (3, 4 * blocks)],
+                   1: [(4, 2 * P), (5, 2 * P)], 3: [(1, P), (3, 4 * blocks), (6, 4 * P)]}[storage]
+    for bid, nb in records:
+        out += struct.pack("<IIQ", bid, 0, nb) + bytes((nb + 7) // 8 * 8)
+    out += struct.pack("<II", 0xFFFFFFFF, len(records))
+    out += struct.pack("<Q", _stream_hash(bytes(out)))
+    return bytes(out)
+
+
+def _load_rc(buf):
+    lib = ma.library()
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_uint8 * len(buf)).from_buffer_copy(buf)
+    rc = lib.adam_state_load(ctypes.byref(h), ctypes.cast(arr, ctypes.c_void_p), len(buf), None)
+    return rc, h.value
+
+
+@pytest.mark.parametrize("mutate", ["magic", "version", "truncate", "checksum", "payload",
+                                    "record_order", "record_size", "storage", "numel"])
+def test_load_rejects_malformed_streams_before_any_device_call(mutate):
+    import struct
+    numels = [5000, 17]
+    good = bytearray(_serialized(numels))
+    if mutate == "magic":
+        bad = b"XEAMSTAT" + bytes(good[8:])
+    elif mutate == "version":
+        bad = _serialized(numels, version=2)
+    elif mutate == "truncate":
+        bad = bytes(good[:-24])
+    elif mutate == "checksum":
+        good[-1] ^= 0x40
+        bad = bytes(good)
+    elif mutate == "payload":
+        good[80] ^= 1  # inside the first record's bytes, checksum now stale
+        bad = bytes(good)
+    elif mutate == "record_order":
+        P = 5008 + 32
+        bad = _serialized(numels, records=[(1, P), (0, P), (2, 16), (3, 16)])
+    elif mutate == "record_size":
+        P = 5008 + 32
+        bad = _serialized(numels, records=[(0, P), (1, P - 16), (2, 16), (3, 16)])
+    elif mutate == "storage":
+        bad = bytearray(good)
+        bad[16:20] = struct.pack("<i", 1)  # claims bf16 but holds 8-bit records
+        bad = bytes(bad[:-8]) + struct.pack("<Q", _stream_hash(bytes(bad[:-8])))
+    else:  # numel
+        bad = bytearray(good)
+        bad[32:40] = struct.pack("<q", -3)
+        bad = bytes(bad[:-8]) + struct.pack("<Q", _stream_hash(bytes(bad[:-8])))
+    rc, h = _load_rc(bytes(bad))
+    assert rc == -1 and h is None, (mutate, ma.adam_last_error())
+
+
+def test_load_of_a_valid_stream_gets_past_validation():
+    # a well-formed stream passes every host check; on a machine without a GPU
+    # the first device call (state creation) is what fails
+    rc, h = _load_rc(_serialized([5000, 17]))
+    if rc == 0:
+        ma.library().adam_state_destroy(h)
+    else:
+        assert rc in (-4, -5), ma.adam_last_error()

@@ -359,3 +359,75 @@ def test_alternating_gradient_buffers_beyond_the_table_cache():
         for nm, want in ost.buffers().items():
             compare_buffer(nm, got[nm], want, True, stats, f"t={t}")
     st.destroy()
+
+
+@pytest.mark.parametrize("storage,gdt,sr,pct", [("bf16", "f32", False, None),
+                                                ("q8", "bf16", True, None),
+                                                ("q8_v_only", "bf16", False, 99.9)])
+def test_checkpoint_resume_is_bit_exact(storage, gdt, sr, pct):
+    # 4 steps, save; continue 3 steps (A); load the checkpoint into a new
+    # state and run the same 3 steps from the saved params (B).  A == B bit
+    # for bit, and both equal the oracle after 7 uninterrupted steps.
+    numels = RAGGED
+    hp = dict(HP, stochastic=sr, percentile=pct, seed=77)
+    params = workloads.host_params(28, numels)
+    dev_p = [torch.from_numpy(x.copy()).cuda() for x in params]
+    st = ma.adam_state_create(numels, storage, gdt)
+    ost = oracle.OracleState(numels, storage, grad_bf16=(gdt == "bf16"))
+    grads = [workloads.host_grads(28, numels, t, dtype=gdt) for t in range(1, 8)]
+    for t in range(1, 5):
+        ma.adam_step(st, dev_p, to_device_grads(grads[t - 1], gdt), t=t, **hp)
+    blob = ma.adam_state_save(st)
+    assert blob.size == ma.adam_state_serialized_bytes(st)
+    saved_p = [x.clone() for x in dev_p]
+    # the stream's records are the state buffers, verbatim
+    got = read_state(st)
+    off = 32 + 8 * len(numels)
+    for name in {"bf16": ["m_bf16", "v_bf16"], "q8": ["m_codes", "v_codes", "m_scale", "v_scale"],
+                 "q8_v_only": ["v_codes", "v_scale", "m_f32"]}[storage]:
+        nb = int(np.frombuffer(blob[off + 8:off + 16].tobytes(), np.uint64)[0])
+        assert nb == got[name].nbytes
+        assert np.array_equal(blob[off + 16:off + 16 + nb], got[name].view(np.uint8)), name
+        off += 16 + (nb + 7) // 8 * 8
+    for t in range(5, 8):
+        ma.adam_step(st, dev_p, to_device_grads(grads[t - 1], gdt), t=t, **hp)
+    st2 = ma.adam_state_load(blob)
+    assert st2.numels == list(numels) and st2.storage == storage
+    for t in range(5, 8):
+        ma.adam_step(st2, saved_p, to_device_grads(grads[t - 1], gdt), t=t, **hp)
+    for t in range(1, 8):
+        ost.step(params, grads[t - 1], t=t, **hp)
+    torch.cuda.synchronize()
+    a, b = read_state(st), read_state(st2)
+    stats = Stats()
+    for nm, want in ost.buffers().items():
+        assert np.array_equal(a[nm].view(np.uint8), b[nm].view(np.uint8)), nm
+        compare_buffer(nm, a[nm], want, sr, stats)
+    for k in range(len(numels)):
+        pa, pb = dev_p[k].cpu().numpy(), saved_p[k].cpu().numpy()
+        assert np.array_equal(pa.view(np.uint32), pb.view(np.uint32))
+        compare_params(pa, params[k], stats)
+    st.destroy()
+    st2.destroy()
+
+
+def test_checkpoint_rejects_a_corrupted_stream():
+    st = ma.adam_state_create([5000, 3], "q8")
+    blob = ma.adam_state_save(st)
+    bad = blob.copy()
+    bad[100] ^= 0x01
+    with pytest.raises(ma.AdamError) as e:
+        ma.adam_state_load(bad)
+    assert e.value.code == -1 and "checksum" in str(e.value)
+    with pytest.raises(ma.AdamError):
+        ma.adam_state_load(blob[:-8])
+    # a destination of the wrong size is refused before any copy
+    rc = ma.library().adam_state_save(ctypes.c_void_p(st.handle), ctypes.c_void_p(blob.ctypes.data),
+                                      blob.size - 8, None)
+    assert rc == -1
+    empty = ma.adam_state_create([], "bf16")
+    again = ma.adam_state_load(ma.adam_state_save(empty))
+    assert again.numels == []
+    st.destroy()
+    empty.destroy()
+    again.destroy()
