@@ -86,9 +86,10 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
         // one 32x32->64 multiply each (v_mad_u64_u32) instead of separate hi/lo
         const uint64_t prod0 = (uint64_t)0xD2511F53u * c[0];
         const uint64_t prod1 = (uint64_t)0xCD9E8D57u * c[2];
-        c[0] = (uint32_t)(prod1 >> 32) ^ c[1] ^ k0;
+        // three-input XOR in one v_bitop3_b32 (truth table 0x96)
+        c[0] = __builtin_amdgcn_bitop3_b32((uint32_t)(prod1 >> 32), c[1], k0, 0x96);
         c[1] = (uint32_t)prod1;
-        c[2] = (uint32_t)(prod0 >> 32) ^ c[3] ^ k1;
+        c[2] = __builtin_amdgcn_bitop3_b32((uint32_t)(prod0 >> 32), c[3], k1, 0x96);
         c[3] = (uint32_t)prod0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
@@ -204,27 +205,26 @@ __device__ uint32_t block_select(const uint32_t (&key)[kItems], uint32_t rank, u
 
 // ---------------------------------------------------------------- quantizer
 // Code magnitude for |x| = a with statistic A and r = fl(qmax/A) (A >= kTiny).
-// With the absmax statistic and nearest-even rounding, a <= A always holds and
-// r = (qmax/A)(1+d), |d| <= 2^-24, so fl(a*r) <= qmax*(1 + 2^-23) and rounds to
-// at most qmax, reaching it at a = A: the end pin and the clamp are then no-ops
-// and are skipped (kClip = false).  Percentile statistics (a may exceed A) and
-// stochastic rounding (floor of a value just below qmax) keep both.
-template <bool kSR, bool kClip>
-__device__ __forceinline__ float code_magnitude(float a, float A, float r, float qmax, uint32_t u16) {
+// For a < A, a <= A(1 - 2^-24) and r <= (qmax/A)(1 + 2^-24), so y = fl(a*r) <=
+// qmax: neither rounding can pass qmax (at y = qmax the fraction is 0), and
+// only a >= A -- possible with the percentile statistic, or at the block
+// maximum under stochastic rounding, where y may fall just below qmax --
+// needs the end pin (kPin).
+//
+// Stochastic rounding: floor(y) + [u16 * 2^-16 < frac(y)] is computed as
+// (ceil(y * 2^16) + 65535 - u16) >> 16.  With Y = y * 2^16 (exact, Y < 2^24)
+// = 2^16 floor(y) + F, u16 < F holds iff u16 < ceil(F), iff the low 16 bits of
+// ceil(Y) + 65535 - u16 carry into bit 16.
+template <bool kSR, bool kPin>
+__device__ __forceinline__ uint32_t code_magnitude(float a, float A, float r, uint32_t qmax, uint32_t u16) {
     const float y = a * r;
-    float k;
+    uint32_t k;
     if constexpr (kSR) {
-        const float down = floorf(y);
-        const float frac = y - down;
-        const float u = (float)u16 * 0x1p-16f;
-        k = down + (u < frac ? 1.0f : 0.0f);
+        k = ((uint32_t)ceilf(y * 65536.0f) + (0xFFFFu - u16)) >> 16;
     } else {
-        k = rintf(y);
+        k = (uint32_t)rintf(y);
     }
-    if constexpr (kClip) {
-        k = fminf(k, qmax);
-        k = a >= A ? qmax : k;
-    }
+    if constexpr (kPin) k = a >= A ? qmax : k;
     return k;
 }
 
@@ -453,10 +453,14 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
             Avn = sv < kTiny ? vmax : sv;
         }
-        constexpr bool kClip = kSR || kPct;
+        constexpr bool kPin = kSR || kPct;
         const bool mzero = !(Amn >= kTiny), vzero = !(Avn >= kTiny);
         const float rm = mzero ? 0.0f : 127.0f / Amn;
         const float rv = vzero ? 0.0f : 255.0f / Avn;
+        // a zero block has r = 0, so y = 0 and every code is 0; its pin
+        // threshold is +inf so that the end pin never fires
+        const float pin_m = mzero ? __builtin_inff() : Amn;
+        const float pin_v = vzero ? __builtin_inff() : Avn;
 
         // ---- requantize and store codes
 #pragma unroll
@@ -474,9 +478,15 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             uint32_t cv = 0;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float q = vzero ? 0.0f
-                                      : code_magnitude<kSR, kClip>(fabsf(vo[4 * j + k]), Avn, rv, 255.0f, w[k] >> 16);
-                cv |= ((uint32_t)q) << (8 * k);
+                const float av = fabsf(vo[4 * j + k]);
+                if constexpr (kSR) {
+                    const uint32_t q = code_magnitude<true, true>(av, pin_v, rv, 255u, w[k] >> 16);
+                    cv |= q << (8 * k);
+                } else {
+                    // nearest-even rounding, clamped to [0, 255], packed into byte k: the
+                    // clamp is the end pin (|v| >= A gives y >= 254.99998)
+                    cv = __builtin_amdgcn_cvt_pk_u8_f32(av * rv, k, cv);
+                }
             }
             st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s, cv);
             if constexpr (kQuantM) {
@@ -484,10 +494,9 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const float x = mo[4 * j + k];
-                    const float q = mzero ? 0.0f
-                                          : code_magnitude<kSR, kClip>(fabsf(x), Amn, rm, 127.0f, w[k] & 0xFFFFu);
-                    const int32_t qs = (int32_t)copysignf(q, x);  // -0 converts to 0
-                    cm |= ((uint32_t)qs & 0xFFu) << (8 * k);
+                    const uint32_t q = code_magnitude<kSR, kPin>(fabsf(x), pin_m, rm, 127u, w[k] & 0xFFFFu);
+                    const uint32_t qs = x < 0.0f ? 0u - q : q;  // -0 gives 0
+                    cm |= (qs & 0xFFu) << (8 * k);
                 }
                 st_u32(reinterpret_cast<int8_t *>(a.m_state) + s, cm);
             } else {
