@@ -60,14 +60,16 @@ def lib():
         [ctypes.c_int32, _i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
         + [_vp] * 8
         + [ctypes.c_float] * 6
-        + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64]
+        + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+           ctypes.c_uint64]
         + [_vp, _vp])
     L.orc_adam_step.restype = ctypes.c_int
     L.orc_adam_step_blocks.argtypes = (
         [ctypes.c_int64, _i64p, _i64p, _i64p, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
         + [_vp] * 8
         + [ctypes.c_float] * 6
-        + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64])
+        + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+           ctypes.c_uint64])
     L.orc_adam_step_blocks.restype = ctypes.c_int
     _lib = L
     return L
@@ -215,11 +217,12 @@ class OracleState:
 
     def step(self, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
              decoupled=True, stochastic=False, percentile=None, seed=42,
-             want_moments=False):
+             static_scales=False, want_moments=False):
         """Advance params (list of float32 arrays, updated in place).
 
         grads: float32 arrays, or uint16 bf16 bit patterns if grad_bf16.
-        percentile=None selects the absmax statistic.
+        percentile=None selects the absmax statistic; static_scales keeps
+        each block's first scale.
         Returns (m_new, v_new) flat padded fp32 arrays if want_moments.
         """
         n = len(self.numels)
@@ -244,7 +247,7 @@ class OracleState:
             _vptr(self.m_codes), _vptr(self.v_codes), _vptr(self.m_scale), _vptr(self.v_scale),
             _vptr(self.m_bf16), _vptr(self.v_bf16), _vptr(self.m_f32), _vptr(self.v_f32),
             lr, beta1, beta2, eps, weight_decay, percentile if use_pct else 100.0,
-            t, int(decoupled), int(stochastic), int(use_pct), seed,
+            t, int(decoupled), int(stochastic), int(use_pct), int(static_scales), seed,
             _vptr(m_new), _vptr(v_new))
         if rc != 0:
             raise ValueError("oracle rejected the step arguments")
@@ -297,7 +300,7 @@ class OracleBlocks:
         return slice(o, o + int(self.n[i]))
 
     def step(self, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
-             decoupled=True, stochastic=False, percentile=None, seed=42):
+             decoupled=True, stochastic=False, percentile=None, seed=42, static_scales=False):
         """params[i]/grads[i]: arrays of block i (params updated in place)."""
         B = len(self.n)
         gdt = np.uint16 if self.grad_bf16 else np.float32
@@ -315,6 +318,6 @@ class OracleBlocks:
             _vptr(s.m_codes), _vptr(s.v_codes), _vptr(s.m_scale), _vptr(s.v_scale),
             _vptr(s.m_bf16), _vptr(s.v_bf16), _vptr(s.m_f32), _vptr(s.v_f32),
             lr, beta1, beta2, eps, weight_decay, percentile if use_pct else 100.0,
-            t, int(decoupled), int(stochastic), int(use_pct), seed)
+            t, int(decoupled), int(stochastic), int(use_pct), int(static_scales), seed)
         if rc != 0:
             raise ValueError("oracle rejected the step arguments")

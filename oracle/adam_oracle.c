@@ -36,7 +36,9 @@
  * torch.optim.AdamW, exhaustive round-trip / fixed-point / constant-block
  * properties of the codebook, brute-force nearest-code search, exhaustive
  * stochastic-rounding draw counts, numpy.percentile(method="lower"), the
- * PyTorch bf16 cast, and PyTorch's header-only Philox engine.
+ * PyTorch bf16 cast, and PyTorch's header-only Philox engine.  Static scales:
+ * first step equal to the dynamic one, scales unchanged once set, later codes
+ * nearest in the codebook of the kept scale (brute force).
  * Parity unpinned: the absolute values of a multi-step trajectory beyond what
  * the composition test of one step from a non-zero state pins (the pages
  * print no worked example).
@@ -276,9 +278,23 @@ enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8 = 2, ORC_Q8_V_ONLY = 3 };
 typedef struct {
     float lr, beta1, beta2, eps, wd, pct;
     int64_t t;
-    int32_t decoupled, stochastic, use_pct;
+    int32_t decoupled, stochastic, use_pct, static_scales;
     uint64_t seed;
 } orc_hparams;
+
+/* Scale of one quantized moment of a block [P814, walkthrough, the options
+   class: UseDynamicQuantization, on by default, chooses scales that follow
+   the moments through training].  Dynamic: the statistic of the new values,
+   every step.  Static (our reading of the option switched off): the scale
+   found the first time the block is quantized (stored scale still 0) is
+   kept; later values at or beyond it saturate to the end of the alphabet. */
+static float quantize_moment(const float *x, int64_t n, int32_t is_signed, const orc_hparams *h,
+                             float stored, const uint16_t *draws, int32_t *codes)
+{
+    if (h->static_scales && stored >= ORC_TINY)
+        return orc_quantize_with_stat(x, n, is_signed, stored, draws, codes);
+    return orc_quantize_block(x, n, is_signed, h->use_pct, h->pct, draws, codes);
+}
 
 /* One element of the update; m_old/v_old are already dequantized. */
 static void adam_element(float p, float g, float m_old, float v_old, const orc_hparams *h,
@@ -357,7 +373,7 @@ static void step_block(float *p, const float *g32, const uint16_t *g16, int64_t 
         if (storage == ORC_Q8) {
             if (draws)
                 orc_sr_draws(h->seed, h->t, gidx, n, 0, draws);
-            ms[0] = orc_quantize_block(m_new, n, 1, h->use_pct, h->pct, draws, codes);
+            ms[0] = quantize_moment(m_new, n, 1, h, ms[0], draws, codes);
             for (int64_t j = 0; j < n; j++)
                 mq[j] = (int8_t)codes[j];
         } else {
@@ -366,7 +382,7 @@ static void step_block(float *p, const float *g32, const uint16_t *g16, int64_t 
         }
         if (draws)
             orc_sr_draws(h->seed, h->t, gidx, n, 1, draws);
-        vs[0] = orc_quantize_block(v_new, n, 0, h->use_pct, h->pct, draws, codes);
+        vs[0] = quantize_moment(v_new, n, 0, h, vs[0], draws, codes);
         for (int64_t j = 0; j < n; j++)
             vq[j] = (uint8_t)codes[j];
         free(codes);
@@ -390,14 +406,15 @@ int orc_adam_step(int32_t n_tensors, const int64_t *numels, int32_t block,
                   float *m_scale, float *v_scale, uint16_t *m_bf16, uint16_t *v_bf16,
                   float *m_f32, float *v_f32, float lr, float beta1, float beta2,
                   float eps, float wd, float pct, int64_t t, int32_t decoupled,
-                  int32_t stochastic, int32_t use_pct, uint64_t seed,
+                  int32_t stochastic, int32_t use_pct, int32_t static_scales, uint64_t seed,
                   float *m_new_out, float *v_new_out)
 {
     if (n_tensors < 0 || block <= 0 || t < 1 || storage < ORC_F32 || storage > ORC_Q8_V_ONLY)
         return -1;
     if (!(pct >= 0.0f && pct <= 100.0f))
         return -1;
-    const orc_hparams h = {lr, beta1, beta2, eps, wd, pct, t, decoupled, stochastic, use_pct, seed};
+    const orc_hparams h = {lr, beta1, beta2, eps, wd, pct, t, decoupled, stochastic, use_pct,
+                           static_scales, seed};
     float s[5];
     orc_host_scalars(lr, beta1, beta2, wd, t, decoupled, s);
 
@@ -438,13 +455,14 @@ int orc_adam_step_blocks(int64_t n_blocks, const int64_t *n, const int64_t *gidx
                          uint16_t *m_bf16, uint16_t *v_bf16, float *m_f32, float *v_f32,
                          float lr, float beta1, float beta2, float eps, float wd, float pct,
                          int64_t t, int32_t decoupled, int32_t stochastic, int32_t use_pct,
-                         uint64_t seed)
+                         int32_t static_scales, uint64_t seed)
 {
     if (n_blocks < 0 || t < 1 || storage < ORC_F32 || storage > ORC_Q8_V_ONLY)
         return -1;
     if (!(pct >= 0.0f && pct <= 100.0f))
         return -1;
-    const orc_hparams h = {lr, beta1, beta2, eps, wd, pct, t, decoupled, stochastic, use_pct, seed};
+    const orc_hparams h = {lr, beta1, beta2, eps, wd, pct, t, decoupled, stochastic, use_pct,
+                           static_scales, seed};
     float s[5];
     orc_host_scalars(lr, beta1, beta2, wd, t, decoupled, s);
     for (int64_t i = 0; i < n_blocks; i++) {
