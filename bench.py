@@ -66,7 +66,7 @@ def traffic_for(workload):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(cfg, steps=1):
+def cpu_baseline(cfg, hp, steps=1):
     """The oracle, as it is, on one full step of the same workload (single
     thread), same recipe of inputs generated on the host."""
     import numpy as np  # noqa: F401
@@ -80,7 +80,7 @@ def cpu_baseline(cfg, steps=1):
         grads = workloads.host_grads(cfg.cfg_id, numels, t, dist=cfg.grad_dist,
                                      dtype=cfg.grad_dtype)
         t0 = time.perf_counter()
-        st.step(params, grads, t=t, **cfg.hp)
+        st.step(params, grads, t=t, **hp)
         elapsed += time.perf_counter() - t0
     n = sum(numels)
     return {"value": round(n * steps / elapsed / 1e9, 5), "unit": "Gparams/s", "cores": 1,
@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--grad-buffers", type=int, default=4,
                     help="distinct pre-generated gradient sets used in rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--static-scales", action="store_true",
+                    help="8-bit sets: keep each block's scale once set")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's device copy of 4 GiB (counter calibration run)")
     args = ap.parse_args()
@@ -133,6 +135,10 @@ def main():
     st = ma.adam_state_create(numels, cfg.storage, cfg.grad_dtype)
     stream = torch.cuda.current_stream()
     hp = dict(cfg.hp)
+    if args.static_scales:
+        if cfg.storage == "bf16":
+            sys.exit("bench.py: --static-scales applies to 8-bit storage only")
+        hp["static_scales"] = True
 
     t = 0
     for _ in range(args.warmup):
@@ -154,7 +160,8 @@ def main():
 
     alg = algorithmic_bytes(cfg)
     achieved = alg / sec / 1e9
-    traffic = traffic_for(cfg.name)
+    # counter readings are taken per workload for the dynamic-scale kernel
+    traffic = None if args.static_scales else traffic_for(cfg.name)
     out = {
         "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",
         "value": round(n_params / sec / 1e9, 3),
@@ -178,6 +185,7 @@ def main():
             "grad_dtype": cfg.grad_dtype,
             "stochastic_rounding": bool(hp.get("stochastic")),
             "percentile": hp.get("percentile"),
+            "static_scales": bool(hp.get("static_scales")),
             "block_size": 2048,
         },
         "roofline": {
@@ -194,7 +202,7 @@ def main():
     del params, gsets
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        out["cpu_baseline"] = cpu_baseline(cfg, hp)
     print(json.dumps(out), flush=True)
 
 

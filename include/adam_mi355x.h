@@ -81,7 +81,15 @@ enum adam_grad_dtype { ADAM_GRAD_F32 = 0, ADAM_GRAD_BF16 = 1 };
 enum adam_flags {
     ADAM_F_DECOUPLED_WD = 1u, /* AdamW (p *= 1 - lr*wd); else Adam with L2 (g += wd*p) */
     ADAM_F_STOCHASTIC = 2u,   /* 8-bit storage only: Philox stochastic rounding; else nearest-even */
-    ADAM_F_PERCENTILE = 4u    /* 8-bit storage only: percentile block statistic; else absmax */
+    ADAM_F_PERCENTILE = 4u,   /* 8-bit storage only: percentile block statistic; else absmax */
+    /* 8-bit storage only: static scales.  The 8-bit Adam page's options class
+     * turns dynamic quantization (scales that follow the moments, the default)
+     * on or off; off is read as: a block's scale is set by the first step that
+     * quantizes it with a statistic >= 2^-112 (its stored scale still 0) and
+     * is kept from then on; moment values at or beyond a kept scale take the
+     * end code (+-127, 255).  Such blocks skip the block statistic.  Steps
+     * with and without this flag may be mixed on one state. */
+    ADAM_F_STATIC_SCALES = 8u
 };
 
 enum adam_buffer {
@@ -154,9 +162,9 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
  *   from the layout given at create returns EMODE (no work enqueued).
  * Errors (no work enqueued): EINVAL (NULL state/params/grads/hp/expect,
  * hyperparameter outside its domain, unknown flag bits, reserved != 0,
- * STOCHASTIC or PERCENTILE with BF16 storage, call from a device other than
- * the one the state was created on), EMODE, EALIGN; EDEVICE if the launch
- * fails.  Device faults surface on the caller's next synchronization.
+ * STOCHASTIC, PERCENTILE or STATIC_SCALES with BF16 storage, call from a
+ * device other than the one the state was created on), EMODE, EALIGN;
+ * EDEVICE if the launch fails.  Device faults surface on the caller's next synchronization.
  */
 int adam_step(adam_state *s, float *const *params, const void *const *grads,
               const adam_hparams *hp, const adam_layout *expect, void *hip_stream);

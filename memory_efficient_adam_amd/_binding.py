@@ -10,7 +10,7 @@ STORAGES = {"bf16": 1, "q8": 2, "q8_v_only": 3}
 GRAD_DTYPES = {"f32": 0, "bf16": 1}
 BUFFERS = {"m_codes": 0, "v_codes": 1, "m_scale": 2, "v_scale": 3, "m_bf16": 4,
            "v_bf16": 5, "m_f32": 6}
-_F_DECOUPLED, _F_STOCHASTIC, _F_PERCENTILE = 1, 2, 4
+_F_DECOUPLED, _F_STOCHASTIC, _F_PERCENTILE, _F_STATIC_SCALES = 1, 2, 4, 8
 _STATUS = {0: "ADAM_OK", -1: "ADAM_EINVAL", -2: "ADAM_EMODE", -3: "ADAM_EALIGN",
            -4: "ADAM_ENOMEM", -5: "ADAM_EDEVICE"}
 
@@ -155,19 +155,21 @@ def adam_state_destroy(state):
 
 
 def adam_step(state, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
-              decoupled=True, stochastic=False, percentile=None, seed=42, stream=None,
-              expect=None):
+              decoupled=True, stochastic=False, percentile=None, seed=42, static_scales=False,
+              stream=None, expect=None):
     """One step over all tensors.  params: fp32 device tensors (updated in
     place); grads: fp32 or bf16 device tensors; percentile=None selects the
-    absmax block statistic.  expect: (storage, grad_dtype[, block_size]) the
-    caller believes the state has (default: the state's own layout)."""
+    absmax block statistic; static_scales keeps each block's scale once set.
+    expect: (storage, grad_dtype[, block_size]) the caller believes the state
+    has (default: the state's own layout)."""
     n = len(state.numels)
     if len(params) != n or len(grads) != n:
         raise ValueError(f"expected {n} params and grads")
     P = (ctypes.c_void_p * max(n, 1))(*[p.data_ptr() for p in params])
     G = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
-    flags = (_F_DECOUPLED if decoupled else 0) | (_F_STOCHASTIC if stochastic else 0) | (
-        _F_PERCENTILE if percentile is not None else 0)
+    flags = ((_F_DECOUPLED if decoupled else 0) | (_F_STOCHASTIC if stochastic else 0)
+             | (_F_PERCENTILE if percentile is not None else 0)
+             | (_F_STATIC_SCALES if static_scales else 0))
     hp = adam_hparams(lr, beta1, beta2, eps, weight_decay,
                       100.0 if percentile is None else percentile, int(t), flags, 0, int(seed))
     lay = state.layout if expect is None else _layout(*expect)

@@ -60,6 +60,7 @@ struct Variant {
     bool grad_bf16;
     bool stochastic;
     bool percentile;
+    bool static_scales;  // keep a block's scale once set (8-bit storage)
 };
 
 // Enqueues the step kernel over every descriptor.

@@ -359,7 +359,9 @@ struct SelectLds<true> {
 };
 
 // Decode, update, store params; block statistic; requantize and store state.
-template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kFull>
+// kStatic: a moment whose stored scale is already set (>= kTiny) keeps it and
+// skips its statistic; values at or beyond it saturate through the end pin.
+template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kFull>
 __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx &c,
                                               const BlockRegs<kStore, kGradBf16> &r, BlockLds &lds,
                                               SelectLds<kPct> &sel) {
@@ -436,24 +438,38 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             }
         }
     } else {
-        // ---- block statistic
-        block_max2(mmax, vmax, lds.red);
-        float Amn = mmax, Avn = vmax;
+        // ---- block statistic (the old scales are block-uniform: every lane
+        // read the same word, so readfirstlane makes the branches scalar)
+        bool keep_m = false, keep_v = false;
+        float Am_old = 0.0f, Av_old = 0.0f;
+        if constexpr (kStatic) {
+            Av_old = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, r.Av)));
+            keep_v = Av_old >= kTiny;
+            if constexpr (kQuantM) {
+                Am_old = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, r.Am)));
+                keep_m = Am_old >= kTiny;
+            }
+        }
+        const bool need_m = kQuantM && !keep_m, need_v = !keep_v;
+        if (need_m || need_v) block_max2(mmax, vmax, lds.red);
+        float Amn = keep_m ? Am_old : mmax, Avn = keep_v ? Av_old : vmax;
         if constexpr (kPct) {
             const uint32_t rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
             uint32_t key[kItems];
-            if constexpr (kQuantM) {
+            if (need_m) {
 #pragma unroll
                 for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(mo[i]) & 0x7FFFFFFFu;
                 const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
                 Amn = sv < kTiny ? mmax : sv;
             }
+            if (need_v) {
 #pragma unroll
-            for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(vo[i]) & 0x7FFFFFFFu;
-            const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
-            Avn = sv < kTiny ? vmax : sv;
+                for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(vo[i]) & 0x7FFFFFFFu;
+                const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
+                Avn = sv < kTiny ? vmax : sv;
+            }
         }
-        constexpr bool kPin = kSR || kPct;
+        constexpr bool kPin = kSR || kPct || kStatic;
         const bool mzero = !(Amn >= kTiny), vzero = !(Avn >= kTiny);
         const float rm = mzero ? 0.0f : 127.0f / Amn;
         const float rv = vzero ? 0.0f : 255.0f / Avn;
@@ -504,9 +520,11 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                          f32x4{mo[4 * j], mo[4 * j + 1], mo[4 * j + 2], mo[4 * j + 3]});
             }
         }
+        // a kept scale is not rewritten: with no statistic there is no
+        // barrier between the waves' reads of it and this store
         if (tid == 0) {
-            if constexpr (kQuantM) a.m_scale[c.slot] = mzero ? 0.0f : Amn;
-            a.v_scale[c.slot] = vzero ? 0.0f : Avn;
+            if (need_m) a.m_scale[c.slot] = mzero ? 0.0f : Amn;
+            if (need_v) a.v_scale[c.slot] = vzero ? 0.0f : Avn;
         }
     }
 }
@@ -515,7 +533,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 // One workgroup per block; workgroups beyond the grid limit loop (stride =
 // grid size).  Descriptors [0, n_full) are full blocks, whose path has no
 // tail checks; the rest are the tensors' ragged last blocks.
-template <int kStore, bool kGradBf16, bool kSR, bool kPct>
+template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic>
 __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
     __shared__ BlockLds lds;
     __shared__ SelectLds<kPct> sel;
@@ -524,10 +542,10 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
         const BlockCtx c = load_ctx<kGradBf16>(a, i);
         if (i < a.n_full) {
             load_data<kStore, kGradBf16, true>(a, c, r);
-            process_block<kStore, kGradBf16, kSR, kPct, true>(a, c, r, lds, sel);
+            process_block<kStore, kGradBf16, kSR, kPct, kStatic, true>(a, c, r, lds, sel);
         } else {
             load_data<kStore, kGradBf16, false>(a, c, r);
-            process_block<kStore, kGradBf16, kSR, kPct, false>(a, c, r, lds, sel);
+            process_block<kStore, kGradBf16, kSR, kPct, kStatic, false>(a, c, r, lds, sel);
         }
         if (i + gridDim.x < a.n_all) __syncthreads();  // LDS reused by the next block
     }
@@ -549,25 +567,31 @@ constexpr int kCuLdsBytes = 160 * 1024;
 constexpr size_t reserve_lds(int resident) { return resident >= 8 ? 0 : kCuLdsBytes / (resident + 1) + 1024; }
 constexpr uint32_t kMaxGrid = (1u << 24) - 1;  // grid.x * 256 work-items < 2^32
 
-template <int kStore, bool kGradBf16, bool kSR, bool kPct>
+template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic = false>
 hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     const uint32_t grid = std::min<uint32_t>(a.n_all, kMaxGrid);
     if (grid == 0) return hipSuccess;
     constexpr int kResident = kStore == kStoreBf16 ? ADAM_BF16_RESIDENT_PER_CU : ADAM_Q8_RESIDENT_PER_CU;
-    constexpr size_t kStatic = sizeof(BlockLds) + sizeof(SelectLds<kPct>);
-    constexpr size_t kDyn = reserve_lds(kResident) > kStatic ? reserve_lds(kResident) - kStatic : 0;
-    hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct>), dim3(grid), dim3(kThreads), kDyn,
+    constexpr size_t kStaticLds = sizeof(BlockLds) + sizeof(SelectLds<kPct>);
+    constexpr size_t kDyn = reserve_lds(kResident) > kStaticLds ? reserve_lds(kResident) - kStaticLds : 0;
+    hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct, kStatic>), dim3(grid), dim3(kThreads), kDyn,
                        stream, a);
     return hipGetLastError();
 }
 
+template <int kStore, bool kGradBf16, bool kStatic>
+hipError_t launch_rounding(const Variant &v, const StepArgs &a, hipStream_t stream) {
+    if (v.stochastic)
+        return v.percentile ? launch_one<kStore, kGradBf16, true, true, kStatic>(a, stream)
+                            : launch_one<kStore, kGradBf16, true, false, kStatic>(a, stream);
+    return v.percentile ? launch_one<kStore, kGradBf16, false, true, kStatic>(a, stream)
+                        : launch_one<kStore, kGradBf16, false, false, kStatic>(a, stream);
+}
+
 template <int kStore, bool kGradBf16>
 hipError_t launch_q(const Variant &v, const StepArgs &a, hipStream_t stream) {
-    if (v.stochastic)
-        return v.percentile ? launch_one<kStore, kGradBf16, true, true>(a, stream)
-                            : launch_one<kStore, kGradBf16, true, false>(a, stream);
-    return v.percentile ? launch_one<kStore, kGradBf16, false, true>(a, stream)
-                        : launch_one<kStore, kGradBf16, false, false>(a, stream);
+    return v.static_scales ? launch_rounding<kStore, kGradBf16, true>(v, a, stream)
+                           : launch_rounding<kStore, kGradBf16, false>(v, a, stream);
 }
 
 }  // namespace

@@ -110,13 +110,13 @@ int check_hparams(const adam_hparams *hp, int32_t storage) {
     if (!(hp->eps > 0.0f) || !is_finite(hp->eps)) return fail(ADAM_EINVAL, "eps must be finite and > 0");
     if (!(hp->weight_decay >= 0.0f) || !is_finite(hp->weight_decay))
         return fail(ADAM_EINVAL, "weight_decay must be finite and >= 0");
-    const uint32_t known = ADAM_F_DECOUPLED_WD | ADAM_F_STOCHASTIC | ADAM_F_PERCENTILE;
+    const uint32_t known = ADAM_F_DECOUPLED_WD | ADAM_F_STOCHASTIC | ADAM_F_PERCENTILE | ADAM_F_STATIC_SCALES;
     if (hp->flags & ~known) return fail(ADAM_EINVAL, "unknown flag bits");
     if (hp->reserved != 0) return fail(ADAM_EINVAL, "reserved must be 0");
     if ((hp->flags & ADAM_F_PERCENTILE) && !(hp->percentile >= 0.0f && hp->percentile <= 100.0f))
         return fail(ADAM_EINVAL, "percentile must be in [0, 100]");
-    if (storage == ADAM_STORE_BF16 && (hp->flags & (ADAM_F_STOCHASTIC | ADAM_F_PERCENTILE)))
-        return fail(ADAM_EINVAL, "stochastic rounding and percentile scaling apply to 8-bit storage only");
+    if (storage == ADAM_STORE_BF16 && (hp->flags & (ADAM_F_STOCHASTIC | ADAM_F_PERCENTILE | ADAM_F_STATIC_SCALES)))
+        return fail(ADAM_EINVAL, "stochastic rounding, percentile and static scales apply to 8-bit storage only");
     return ADAM_OK;
 }
 
@@ -606,7 +606,7 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
     a.n_full = (uint32_t)s->n_full;
     a.n_all = (uint32_t)s->nblocks;
     Variant v{s->layout.storage, s->layout.grad_dtype == ADAM_GRAD_BF16, (hp->flags & ADAM_F_STOCHASTIC) != 0,
-              (hp->flags & ADAM_F_PERCENTILE) != 0};
+              (hp->flags & ADAM_F_PERCENTILE) != 0, (hp->flags & ADAM_F_STATIC_SCALES) != 0};
     if ((e = launch_step(v, a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
     return ADAM_OK;
 }

@@ -9,11 +9,14 @@ gets and compares element by element (criteria in tests/parity.py):
   * the full-size ViT-Base, GPT-1.3B and Llama-7B shaped sets in the
     benchmark's launch configuration, on a sample of blocks that includes
     every tail block;
+  * static scales (kept once set) on the ragged set, mixed with dynamic
+    steps, and on the full-size Llama-7B set;
   * edge cases: empty lists and zero-size tensors, a 2^32-1 element tensor,
     injected non-zero states, degenerate hyperparameters, pointer changes,
     a side stream, and the error paths.
 """
 import ctypes
+import dataclasses
 import sys
 
 import numpy as np
@@ -77,6 +80,54 @@ def test_ragged_set_every_mode(storage, gdt, sr, pct, dec):
         log(f"  {dist}: {stats}")
 
 
+STATIC_MODES = [
+    # storage, grad dtype, stochastic, percentile
+    ("q8", "f32", False, None),
+    ("q8", "bf16", True, None),
+    ("q8", "f32", False, 99.9),
+    ("q8", "bf16", True, 99.9),
+    ("q8_v_only", "f32", False, None),
+    ("q8_v_only", "bf16", True, 99.9),
+]
+
+
+@pytest.mark.parametrize("storage,gdt,sr,pct", STATIC_MODES)
+def test_ragged_set_static_scales(storage, gdt, sr, pct):
+    log(f"ragged static scales {storage} grads={gdt} sr={sr} pct={pct}")
+    hp = dict(HP, stochastic=sr, percentile=pct, static_scales=True, seed=99)
+    for dist in ("normal", "student_t3"):
+        stats = run_full_parity(RAGGED, storage, gdt, 10, hp, cfg_id=12, grad_dist=dist)
+        log(f"  {dist}: {stats}")
+
+
+@pytest.mark.parametrize("storage", ["q8", "q8_v_only"])
+def test_static_scales_set_late_and_mixed_with_dynamic_steps(storage):
+    # tensor 1 sees zero gradients for two steps (its blocks stay unscaled),
+    # and static and dynamic steps alternate on one state
+    numels = RAGGED
+    log(f"static/dynamic mix {storage}")
+    params = workloads.host_params(13, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, storage, "f32")
+    ost = oracle.OracleState(numels, storage)
+    stats = Stats()
+    for t, static in enumerate([True, True, True, False, True, True, False, False, True], start=1):
+        grads = workloads.host_grads(13, numels, t)
+        if t <= 2:
+            grads[1] = np.zeros_like(grads[1])
+        hp = dict(HP, static_scales=static, stochastic=(t % 3 == 0), seed=5)
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t} tensor {k}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, hp["stochastic"], stats, f"t={t}")
+    log(f"  {stats}")
+    st.destroy()
+
+
 def test_single_tensor_1m_q8_ten_steps():
     cfg = workloads.CONFIGS["single_q8"]
     log("single 1M q8 nearest-even, 10 steps")
@@ -84,6 +135,14 @@ def test_single_tensor_1m_q8_ten_steps():
                             cfg_id=cfg.cfg_id)
     log(f"  {stats}")
     assert stats.params == 10 * 1048576
+
+
+def test_full_size_sampled_blocks_static_scales():
+    cfg = dataclasses.replace(workloads.CONFIGS["llama7b_mf32_vq8_pct"], steps=4)
+    cfg.hp = dict(cfg.hp, static_scales=True)
+    log(f"full-size {cfg.name} static scales: {sum(cfg.numels())} params, {cfg.steps} steps")
+    stats = run_sampled_parity(cfg, log=log)
+    assert stats.codes >= stats.params >= cfg.steps * 800 * 1024
 
 
 @pytest.mark.parametrize("name", ["vit_bf16", "vit_q8", "gpt1p3b_q8_sr",
@@ -321,6 +380,9 @@ def test_error_paths_enqueue_nothing():
     bst = ma.adam_state_create(numels, "bf16")
     with pytest.raises(ma.AdamError):
         ma.adam_step(bst, [p[:100]], [g[:100]], t=1, stochastic=True, **HP)
+    with pytest.raises(ma.AdamError) as e:
+        ma.adam_step(bst, [p[:100]], [g[:100]], t=1, static_scales=True, **HP)
+    assert e.value.code == -1
     with pytest.raises(ma.AdamError):
         ma.adam_state_read(bst, "m_codes")
     lib = ma.library()
