@@ -21,6 +21,14 @@ from . import build as _build
 _STORAGE = {"f32": 0, "bf16": 1, "q8": 2, "q8_v_only": 3}
 _lib = None
 
+# state buffers, in the order of the C struct orc_ptrs
+_PTR_FIELDS = ["m_codes", "v_codes", "vmax_codes", "m_scale", "v_scale", "vmax_scale",
+               "m_bf16", "v_bf16", "vmax_bf16", "m_f32", "v_f32", "vmax_f32"]
+
+
+class _OrcPtrs(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in _PTR_FIELDS]
+
 _f32p = ctypes.POINTER(ctypes.c_float)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _u32p = ctypes.POINTER(ctypes.c_uint32)
@@ -57,19 +65,17 @@ def lib():
     L.orc_host_scalars.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                    ctypes.c_float, ctypes.c_int64, ctypes.c_int32, _f32p]
     L.orc_adam_step.argtypes = (
-        [ctypes.c_int32, _i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
-        + [_vp] * 8
+        [ctypes.c_int32, _i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+         ctypes.POINTER(_OrcPtrs)]
         + [ctypes.c_float] * 6
-        + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-           ctypes.c_uint64]
-        + [_vp, _vp])
+        + [ctypes.c_int64] + [ctypes.c_int32] * 5 + [ctypes.c_uint64]
+        + [_vp, _vp, _vp])
     L.orc_adam_step.restype = ctypes.c_int
     L.orc_adam_step_blocks.argtypes = (
-        [ctypes.c_int64, _i64p, _i64p, _i64p, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
-        + [_vp] * 8
+        [ctypes.c_int64, _i64p, _i64p, _i64p, ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+         ctypes.POINTER(_OrcPtrs)]
         + [ctypes.c_float] * 6
-        + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-           ctypes.c_uint64])
+        + [ctypes.c_int64] + [ctypes.c_int32] * 5 + [ctypes.c_uint64])
     L.orc_adam_step_blocks.restype = ctypes.c_int
     _lib = L
     return L
@@ -180,40 +186,25 @@ class OracleState:
       bf16:       m_bf16, v_bf16 (uint16 bit patterns)
       q8:         m_codes (int8), v_codes (uint8), m_scale, v_scale
       q8_v_only:  m_f32, v_codes, v_scale
+    amsgrad adds the running maximum of v, stored like v: vmax_f32,
+    vmax_bf16, or vmax_codes (uint8) + vmax_scale.
     """
 
-    def __init__(self, numels, storage, block=2048, grad_bf16=False):
+    def __init__(self, numels, storage, block=2048, grad_bf16=False, amsgrad=False):
         self.numels = [int(n) for n in numels]
         self.storage = storage
         self.block = int(block)
         self.grad_bf16 = bool(grad_bf16)
+        self.amsgrad = bool(amsgrad)
         self.total = sum(pad16(n) for n in self.numels)
         self.nblocks = sum((n + self.block - 1) // self.block for n in self.numels)
-        T, B = self.total, self.nblocks
-        self.m_f32 = self.v_f32 = self.m_bf16 = self.v_bf16 = None
-        self.m_codes = self.v_codes = self.m_scale = self.v_scale = None
-        if storage == "f32":
-            self.m_f32 = np.zeros(T, np.float32)
-            self.v_f32 = np.zeros(T, np.float32)
-        elif storage == "bf16":
-            self.m_bf16 = np.zeros(T, np.uint16)
-            self.v_bf16 = np.zeros(T, np.uint16)
-        elif storage == "q8":
-            self.m_codes = np.zeros(T, np.int8)
-            self.v_codes = np.zeros(T, np.uint8)
-            self.m_scale = np.zeros(B, np.float32)
-            self.v_scale = np.zeros(B, np.float32)
-        elif storage == "q8_v_only":
-            self.m_f32 = np.zeros(T, np.float32)
-            self.v_codes = np.zeros(T, np.uint8)
-            self.v_scale = np.zeros(B, np.float32)
-        else:
-            raise ValueError(storage)
+        _alloc(self, storage, self.total, self.nblocks, self.amsgrad)
 
     def buffers(self):
-        names = ["m_codes", "v_codes", "m_scale", "v_scale", "m_bf16", "v_bf16",
-                 "m_f32", "v_f32"]
-        return {k: getattr(self, k) for k in names if getattr(self, k) is not None}
+        return {k: getattr(self, k) for k in _PTR_FIELDS if getattr(self, k) is not None}
+
+    def _ptrs(self):
+        return _OrcPtrs(*[_vptr(getattr(self, f)) for f in _PTR_FIELDS])
 
     def step(self, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
              decoupled=True, stochastic=False, percentile=None, seed=42,
@@ -223,7 +214,8 @@ class OracleState:
         grads: float32 arrays, or uint16 bf16 bit patterns if grad_bf16.
         percentile=None selects the absmax statistic; static_scales keeps
         each block's first scale.
-        Returns (m_new, v_new) flat padded fp32 arrays if want_moments.
+        Returns (m_new, v_new) -- plus vmax_new with amsgrad -- flat padded
+        fp32 arrays if want_moments.
         """
         n = len(self.numels)
         assert len(params) == n and len(grads) == n
@@ -236,24 +228,52 @@ class OracleState:
         P = (ctypes.c_void_p * max(n, 1))(*[p.ctypes.data for p in params])
         G = (ctypes.c_void_p * max(n, 1))(*[np.ascontiguousarray(g).ctypes.data
                                              for g in grads])
-        m_new = v_new = None
+        m_new = v_new = w_new = None
         if want_moments:
             m_new = np.zeros(self.total, np.float32)
             v_new = np.zeros(self.total, np.float32)
+            w_new = np.zeros(self.total, np.float32)
         use_pct = percentile is not None
+        ptrs = self._ptrs()
         rc = lib().orc_adam_step(
             n, _ptr(numels, _i64p), self.block, _STORAGE[self.storage], int(self.grad_bf16),
-            ctypes.cast(P, _vp), ctypes.cast(G, _vp),
-            _vptr(self.m_codes), _vptr(self.v_codes), _vptr(self.m_scale), _vptr(self.v_scale),
-            _vptr(self.m_bf16), _vptr(self.v_bf16), _vptr(self.m_f32), _vptr(self.v_f32),
+            ctypes.cast(P, _vp), ctypes.cast(G, _vp), ctypes.byref(ptrs),
             lr, beta1, beta2, eps, weight_decay, percentile if use_pct else 100.0,
-            t, int(decoupled), int(stochastic), int(use_pct), int(static_scales), seed,
-            _vptr(m_new), _vptr(v_new))
+            t, int(decoupled), int(stochastic), int(use_pct), int(static_scales),
+            int(self.amsgrad), seed, _vptr(m_new), _vptr(v_new), _vptr(w_new))
         if rc != 0:
             raise ValueError("oracle rejected the step arguments")
         if want_moments:
-            return m_new, v_new
+            return (m_new, v_new, w_new) if self.amsgrad else (m_new, v_new)
         return None
+
+
+def _alloc(obj, storage, T, B, amsgrad):
+    for f in _PTR_FIELDS:
+        setattr(obj, f, None)
+    if storage == "f32":
+        obj.m_f32 = np.zeros(T, np.float32)
+        obj.v_f32 = np.zeros(T, np.float32)
+        if amsgrad:
+            obj.vmax_f32 = np.zeros(T, np.float32)
+    elif storage == "bf16":
+        obj.m_bf16 = np.zeros(T, np.uint16)
+        obj.v_bf16 = np.zeros(T, np.uint16)
+        if amsgrad:
+            obj.vmax_bf16 = np.zeros(T, np.uint16)
+    elif storage in ("q8", "q8_v_only"):
+        if storage == "q8":
+            obj.m_codes = np.zeros(T, np.int8)
+            obj.m_scale = np.zeros(B, np.float32)
+        else:
+            obj.m_f32 = np.zeros(T, np.float32)
+        obj.v_codes = np.zeros(T, np.uint8)
+        obj.v_scale = np.zeros(B, np.float32)
+        if amsgrad:
+            obj.vmax_codes = np.zeros(T, np.uint8)
+            obj.vmax_scale = np.zeros(B, np.float32)
+    else:
+        raise ValueError(storage)
 
 
 class OracleBlocks:
@@ -264,33 +284,18 @@ class OracleBlocks:
     arrays sized to the sample; scale slot i.
     """
 
-    def __init__(self, blocks, storage, grad_bf16=False):
+    def __init__(self, blocks, storage, grad_bf16=False, amsgrad=False):
         self.n = np.array([b[0] for b in blocks], np.int64)
         self.gidx = np.array([b[1] for b in blocks], np.int64)
         self.off = np.zeros(len(blocks), np.int64)
         if len(blocks):
             self.off[1:] = np.cumsum([pad16(int(x)) for x in self.n])[:-1]
         total = int(sum(pad16(int(x)) for x in self.n))
-        self.inner = OracleState([], storage, grad_bf16=grad_bf16)
+        self.inner = OracleState([], storage, grad_bf16=grad_bf16, amsgrad=amsgrad)
         self.storage = storage
         self.grad_bf16 = bool(grad_bf16)
-        B = len(blocks)
-        s = self.inner
-        if storage == "bf16":
-            s.m_bf16 = np.zeros(total, np.uint16)
-            s.v_bf16 = np.zeros(total, np.uint16)
-        elif storage == "q8":
-            s.m_codes = np.zeros(total, np.int8)
-            s.v_codes = np.zeros(total, np.uint8)
-            s.m_scale = np.zeros(B, np.float32)
-            s.v_scale = np.zeros(B, np.float32)
-        elif storage == "q8_v_only":
-            s.m_f32 = np.zeros(total, np.float32)
-            s.v_codes = np.zeros(total, np.uint8)
-            s.v_scale = np.zeros(B, np.float32)
-        elif storage == "f32":
-            s.m_f32 = np.zeros(total, np.float32)
-            s.v_f32 = np.zeros(total, np.float32)
+        self.amsgrad = bool(amsgrad)
+        _alloc(self.inner, storage, total, len(blocks), self.amsgrad)
 
     def buffers(self):
         return self.inner.buffers()
@@ -309,15 +314,14 @@ class OracleBlocks:
             assert grads[i].dtype == gdt and grads[i].size == self.n[i]
         P = (ctypes.c_void_p * max(B, 1))(*[p.ctypes.data for p in params])
         G = (ctypes.c_void_p * max(B, 1))(*[g.ctypes.data for g in grads])
-        s = self.inner
         use_pct = percentile is not None
+        ptrs = self.inner._ptrs()
         rc = lib().orc_adam_step_blocks(
             B, _ptr(self.n, _i64p), _ptr(self.gidx, _i64p), _ptr(self.off, _i64p),
             _STORAGE[self.storage], int(self.grad_bf16),
-            ctypes.cast(P, _vp), ctypes.cast(G, _vp),
-            _vptr(s.m_codes), _vptr(s.v_codes), _vptr(s.m_scale), _vptr(s.v_scale),
-            _vptr(s.m_bf16), _vptr(s.v_bf16), _vptr(s.m_f32), _vptr(s.v_f32),
+            ctypes.cast(P, _vp), ctypes.cast(G, _vp), ctypes.byref(ptrs),
             lr, beta1, beta2, eps, weight_decay, percentile if use_pct else 100.0,
-            t, int(decoupled), int(stochastic), int(use_pct), int(static_scales), seed)
+            t, int(decoupled), int(stochastic), int(use_pct), int(static_scales),
+            int(self.amsgrad), seed)
         if rc != 0:
             raise ValueError("oracle rejected the step arguments")

@@ -23,6 +23,9 @@
  *           1, 2, 3", SC'11 -- definition of the Philox4x32 bijection.
  *   [KB15]  Kingma & Ba, "Adam: A Method for Stochastic Optimization",
  *           Algorithm 1 (the pages name the update but never print it).
+ *   [RKK18] Reddi, Kale & Kumar, "On the Convergence of Adam and Beyond",
+ *           ICLR 2018 -- AMSGrad, which [P1745] names (the PR description and
+ *           "The real fix": still without a fused kernel) but never prints.
  *
  * Precision: the pages store params and per-block scales as 32-bit floats and
  * moments as bf16 or bytes; every code is an integer decided by fp32
@@ -38,7 +41,10 @@
  * stochastic-rounding draw counts, numpy.percentile(method="lower"), the
  * PyTorch bf16 cast, and PyTorch's header-only Philox engine.  Static scales:
  * first step equal to the dynamic one, scales unchanged once set, later codes
- * nearest in the codebook of the kept scale (brute force).
+ * nearest in the codebook of the kept scale (brute force).  AMSGrad:
+ * torch.optim.AdamW/Adam(amsgrad=True) in the fp32 mode, the running
+ * maximum's draws against PyTorch's Philox engine, one 8-bit step from a
+ * non-zero state composed from pinned parts.
  * Parity unpinned: the absolute values of a multi-step trajectory beyond what
  * the composition test of one step from a non-zero state pins (the pages
  * print no worked example).
@@ -120,21 +126,24 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
 /* Stochastic-rounding draws [P814, key features: "stochastic rounding
    option"].  Reading: element with padded flat index i at step t takes
    word (i mod 4) of Philox4x32-10 with key = (lo32 seed, hi32 seed) and
-   counter = (lo32(i/4), hi32(i/4), lo32 t, hi32 t).  The first moment uses
-   the low 16 bits of that word, the second moment the high 16 bits. */
+   counter = (lo32(c), hi32(c), lo32 t, hi32 t), c = i/4.  The first moment
+   (which 0) uses the low 16 bits of that word, the second moment (which 1)
+   the high 16 bits.  The running maximum of the second moment (AMSGrad,
+   which 2) uses the low 16 bits of the word at c = i/4 + 2^63: flat indices
+   stay below 2^62, so its counters never meet the first stream's. */
 void orc_sr_draws(uint64_t seed, int64_t t, int64_t gidx0, int64_t n,
                   int32_t which, uint16_t *out)
 {
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     for (int64_t j = 0; j < n; j++) {
         const uint64_t i = (uint64_t)(gidx0 + j);
-        const uint64_t grp = i >> 2;
+        const uint64_t grp = (i >> 2) | (which == 2 ? (1ull << 63) : 0ull);
         const uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32),
                                  (uint32_t)(uint64_t)t, (uint32_t)((uint64_t)t >> 32)};
         uint32_t w[4];
         orc_philox4x32_10(ctr, key, w);
         const uint32_t word = w[i & 3u];
-        out[j] = (uint16_t)(which == 0 ? (word & 0xFFFFu) : (word >> 16));
+        out[j] = (uint16_t)(which == 1 ? (word >> 16) : (word & 0xFFFFu));
     }
 }
 
@@ -278,7 +287,7 @@ enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8 = 2, ORC_Q8_V_ONLY = 3 };
 typedef struct {
     float lr, beta1, beta2, eps, wd, pct;
     int64_t t;
-    int32_t decoupled, stochastic, use_pct, static_scales;
+    int32_t decoupled, stochastic, use_pct, static_scales, amsgrad;
     uint64_t seed;
 } orc_hparams;
 
@@ -296,9 +305,13 @@ static float quantize_moment(const float *x, int64_t n, int32_t is_signed, const
     return orc_quantize_block(x, n, is_signed, h->use_pct, h->pct, draws, codes);
 }
 
-/* One element of the update; m_old/v_old are already dequantized. */
-static void adam_element(float p, float g, float m_old, float v_old, const orc_hparams *h,
-                         const float s[5], float *p_new, float *m_new, float *v_new)
+/* One element of the update; m_old/v_old/w_old are already dequantized.
+   AMSGrad [RKK18, Algorithm 2, in PyTorch's convention: the running maximum
+   w of the uncorrected second moment replaces v in the denominator, and the
+   bias correction of v is applied to it]: w = max(w_old, v). */
+static void adam_element(float p, float g, float m_old, float v_old, float w_old,
+                         const orc_hparams *h, const float s[5], float *p_new, float *m_new,
+                         float *v_new, float *w_new)
 {
     const float step = s[0], ibc2 = s[1], decay = s[2], omb1 = s[3], omb2 = s[4];
     if (!h->decoupled)
@@ -306,64 +319,93 @@ static void adam_element(float p, float g, float m_old, float v_old, const orc_h
     const float m = fmaf(h->beta1, m_old, omb1 * g);
     const float gg = g * g;
     const float v = fmaf(h->beta2, v_old, omb2 * gg);
-    const float denom = fmaf(sqrtf(v), ibc2, h->eps);  /* sqrt(v_hat) + eps */
+    const float w = h->amsgrad ? fmaxf(w_old, v) : v;
+    const float denom = fmaf(sqrtf(w), ibc2, h->eps);  /* sqrt(v_hat) + eps */
     const float ratio = m / denom;                      /* m_hat/(...) * bc1 */
     *p_new = fmaf(-step, ratio, p * decay);
     *m_new = m;
     *v_new = v;
+    *w_new = w;
 }
 
 static int64_t pad16(int64_t n) { return (n + 15) / 16 * 16; }
 
+/* State of the elements a step works on: each pointer, if not NULL,
+   points at the first element (scales: the first scale slot) of the range.
+   w* hold the running maximum of the second moment (AMSGrad), stored like v:
+   wf fp32 (F32 mode), wh bf16 (BF16 mode), wq + ws codes and scale (8-bit
+   modes). */
+typedef struct {
+    int8_t *mq;
+    uint8_t *vq, *wq;
+    float *ms, *vs, *ws;
+    uint16_t *mh, *vh, *wh;
+    float *mf, *vf, *wf;
+} orc_ptrs;
+
 /* Per-block worker: n elements of one block whose first padded flat index
-   is gidx.  The state pointers point at the block's first element (and the
-   scale pointers at its scale slot); unused ones may be NULL.  m_new_out /
-   v_new_out, if not NULL, receive the unquantized new moments. */
+   is gidx; q points at the block's state.  m/v/w_new_out, if not NULL,
+   receive the unquantized new moments. */
 static void step_block(float *p, const float *g32, const uint16_t *g16, int64_t n,
                        int64_t gidx, int32_t storage, const orc_hparams *h,
-                       const float s[5], int8_t *mq, uint8_t *vq, float *ms, float *vs,
-                       uint16_t *mh, uint16_t *vh, float *mf, float *vf,
-                       float *m_new_out, float *v_new_out)
+                       const float s[5], const orc_ptrs *q,
+                       float *m_new_out, float *v_new_out, float *w_new_out)
 {
     float *m_new = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
     float *v_new = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    float *w_new = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
     for (int64_t j = 0; j < n; j++) {
         const float gj = g32 ? g32[j] : orc_f32_from_bf16(g16[j]);
-        float m_old, v_old;
+        float m_old, v_old, w_old = 0.0f;
         switch (storage) {
         case ORC_F32:
-            m_old = mf[j];
-            v_old = vf[j];
+            m_old = q->mf[j];
+            v_old = q->vf[j];
+            if (h->amsgrad)
+                w_old = q->wf[j];
             break;
         case ORC_BF16:
-            m_old = orc_f32_from_bf16(mh[j]);
-            v_old = orc_f32_from_bf16(vh[j]);
+            m_old = orc_f32_from_bf16(q->mh[j]);
+            v_old = orc_f32_from_bf16(q->vh[j]);
+            if (h->amsgrad)
+                w_old = orc_f32_from_bf16(q->wh[j]);
             break;
         case ORC_Q8:
-            m_old = orc_dequantize(mq[j], ms[0], 1);
-            v_old = orc_dequantize(vq[j], vs[0], 0);
+            m_old = orc_dequantize(q->mq[j], q->ms[0], 1);
+            v_old = orc_dequantize(q->vq[j], q->vs[0], 0);
+            if (h->amsgrad)
+                w_old = orc_dequantize(q->wq[j], q->ws[0], 0);
             break;
         default: /* ORC_Q8_V_ONLY */
-            m_old = mf[j];
-            v_old = orc_dequantize(vq[j], vs[0], 0);
+            m_old = q->mf[j];
+            v_old = orc_dequantize(q->vq[j], q->vs[0], 0);
+            if (h->amsgrad)
+                w_old = orc_dequantize(q->wq[j], q->ws[0], 0);
             break;
         }
-        adam_element(p[j], gj, m_old, v_old, h, s, &p[j], &m_new[j], &v_new[j]);
+        adam_element(p[j], gj, m_old, v_old, w_old, h, s, &p[j], &m_new[j], &v_new[j],
+                     &w_new[j]);
         if (m_new_out)
             m_new_out[j] = m_new[j];
         if (v_new_out)
             v_new_out[j] = v_new[j];
+        if (w_new_out)
+            w_new_out[j] = w_new[j];
     }
 
     if (storage == ORC_F32) {
         for (int64_t j = 0; j < n; j++) {
-            mf[j] = m_new[j];
-            vf[j] = v_new[j];
+            q->mf[j] = m_new[j];
+            q->vf[j] = v_new[j];
+            if (h->amsgrad)
+                q->wf[j] = w_new[j];
         }
     } else if (storage == ORC_BF16) {
         for (int64_t j = 0; j < n; j++) {
-            mh[j] = orc_bf16_from_f32(m_new[j]);
-            vh[j] = orc_bf16_from_f32(v_new[j]);
+            q->mh[j] = orc_bf16_from_f32(m_new[j]);
+            q->vh[j] = orc_bf16_from_f32(v_new[j]);
+            if (h->amsgrad)
+                q->wh[j] = orc_bf16_from_f32(w_new[j]);
         }
     } else {
         int32_t *codes = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
@@ -373,23 +415,64 @@ static void step_block(float *p, const float *g32, const uint16_t *g16, int64_t 
         if (storage == ORC_Q8) {
             if (draws)
                 orc_sr_draws(h->seed, h->t, gidx, n, 0, draws);
-            ms[0] = quantize_moment(m_new, n, 1, h, ms[0], draws, codes);
+            q->ms[0] = quantize_moment(m_new, n, 1, h, q->ms[0], draws, codes);
             for (int64_t j = 0; j < n; j++)
-                mq[j] = (int8_t)codes[j];
+                q->mq[j] = (int8_t)codes[j];
         } else {
             for (int64_t j = 0; j < n; j++)
-                mf[j] = m_new[j];
+                q->mf[j] = m_new[j];
         }
         if (draws)
             orc_sr_draws(h->seed, h->t, gidx, n, 1, draws);
-        vs[0] = quantize_moment(v_new, n, 0, h, vs[0], draws, codes);
+        q->vs[0] = quantize_moment(v_new, n, 0, h, q->vs[0], draws, codes);
         for (int64_t j = 0; j < n; j++)
-            vq[j] = (uint8_t)codes[j];
+            q->vq[j] = (uint8_t)codes[j];
+        if (h->amsgrad) {
+            /* the running maximum: same alphabet, statistic and rounding as v,
+               its own scale per block and its own draws */
+            if (draws)
+                orc_sr_draws(h->seed, h->t, gidx, n, 2, draws);
+            q->ws[0] = quantize_moment(w_new, n, 0, h, q->ws[0], draws, codes);
+            for (int64_t j = 0; j < n; j++)
+                q->wq[j] = (uint8_t)codes[j];
+        }
         free(codes);
         free(draws);
     }
     free(m_new);
     free(v_new);
+    free(w_new);
+}
+
+/* q advanced to element i0 and scale slot blk (NULL entries stay NULL). */
+static orc_ptrs advance(const orc_ptrs *q, int64_t i0, int64_t blk)
+{
+    orc_ptrs r;
+    r.mq = q->mq ? q->mq + i0 : NULL;
+    r.vq = q->vq ? q->vq + i0 : NULL;
+    r.wq = q->wq ? q->wq + i0 : NULL;
+    r.ms = q->ms ? q->ms + blk : NULL;
+    r.vs = q->vs ? q->vs + blk : NULL;
+    r.ws = q->ws ? q->ws + blk : NULL;
+    r.mh = q->mh ? q->mh + i0 : NULL;
+    r.vh = q->vh ? q->vh + i0 : NULL;
+    r.wh = q->wh ? q->wh + i0 : NULL;
+    r.mf = q->mf ? q->mf + i0 : NULL;
+    r.vf = q->vf ? q->vf + i0 : NULL;
+    r.wf = q->wf ? q->wf + i0 : NULL;
+    return r;
+}
+
+/* The buffers a storage mode needs are all present. */
+static int has_buffers(const orc_ptrs *q, int32_t storage, int32_t amsgrad)
+{
+    switch (storage) {
+    case ORC_F32: return q->mf && q->vf && (!amsgrad || q->wf);
+    case ORC_BF16: return q->mh && q->vh && (!amsgrad || q->wh);
+    case ORC_Q8: return q->mq && q->vq && q->ms && q->vs && (!amsgrad || (q->wq && q->ws));
+    case ORC_Q8_V_ONLY: return q->mf && q->vq && q->vs && (!amsgrad || (q->wq && q->ws));
+    default: return 0;
+    }
 }
 
 /*
@@ -398,23 +481,22 @@ static void step_block(float *p, const float *g32, const uint16_t *g16, int64_t 
  * entries starting at the sum of the earlier segments; its blocks cover
  * local [b*block, min(numel, (b+1)*block)), numbered tensor-major.
  * grads[k] points at fp32 (grad_bf16 == 0) or bf16 bit patterns.
- * Returns 0, or -1 on an argument the step does not define.
+ * m/v/w_new_out, if not NULL, receive the unquantized new moments (flat,
+ * padded).  Returns 0, or -1 on an argument the step does not define.
  */
 int orc_adam_step(int32_t n_tensors, const int64_t *numels, int32_t block,
                   int32_t storage, int32_t grad_bf16, float *const *params,
-                  const void *const *grads, int8_t *m_codes, uint8_t *v_codes,
-                  float *m_scale, float *v_scale, uint16_t *m_bf16, uint16_t *v_bf16,
-                  float *m_f32, float *v_f32, float lr, float beta1, float beta2,
-                  float eps, float wd, float pct, int64_t t, int32_t decoupled,
-                  int32_t stochastic, int32_t use_pct, int32_t static_scales, uint64_t seed,
-                  float *m_new_out, float *v_new_out)
+                  const void *const *grads, const orc_ptrs *state, float lr, float beta1,
+                  float beta2, float eps, float wd, float pct, int64_t t, int32_t decoupled,
+                  int32_t stochastic, int32_t use_pct, int32_t static_scales, int32_t amsgrad,
+                  uint64_t seed, float *m_new_out, float *v_new_out, float *w_new_out)
 {
     if (n_tensors < 0 || block <= 0 || t < 1 || storage < ORC_F32 || storage > ORC_Q8_V_ONLY)
         return -1;
-    if (!(pct >= 0.0f && pct <= 100.0f))
+    if (!(pct >= 0.0f && pct <= 100.0f) || !state || !has_buffers(state, storage, amsgrad))
         return -1;
     const orc_hparams h = {lr, beta1, beta2, eps, wd, pct, t, decoupled, stochastic, use_pct,
-                           static_scales, seed};
+                           static_scales, amsgrad, seed};
     float s[5];
     orc_host_scalars(lr, beta1, beta2, wd, t, decoupled, s);
 
@@ -428,12 +510,10 @@ int orc_adam_step(int32_t n_tensors, const int64_t *numels, int32_t block,
             const float *g32 = grad_bf16 ? NULL : (const float *)grads[k] + b0;
             const uint16_t *g16 = grad_bf16 ? (const uint16_t *)grads[k] + b0 : NULL;
             const int64_t i0 = seg + b0;
-            step_block(params[k] + b0, g32, g16, nb, i0, storage, &h, s,
-                       m_codes ? m_codes + i0 : NULL, v_codes ? v_codes + i0 : NULL,
-                       m_scale ? m_scale + blk : NULL, v_scale ? v_scale + blk : NULL,
-                       m_bf16 ? m_bf16 + i0 : NULL, v_bf16 ? v_bf16 + i0 : NULL,
-                       m_f32 ? m_f32 + i0 : NULL, v_f32 ? v_f32 + i0 : NULL,
-                       m_new_out ? m_new_out + i0 : NULL, v_new_out ? v_new_out + i0 : NULL);
+            const orc_ptrs q = advance(state, i0, blk);
+            step_block(params[k] + b0, g32, g16, nb, i0, storage, &h, s, &q,
+                       m_new_out ? m_new_out + i0 : NULL, v_new_out ? v_new_out + i0 : NULL,
+                       w_new_out ? w_new_out + i0 : NULL);
             blk++;
         }
         seg += pad16(n);
@@ -450,29 +530,24 @@ int orc_adam_step(int32_t n_tensors, const int64_t *numels, int32_t block,
  */
 int orc_adam_step_blocks(int64_t n_blocks, const int64_t *n, const int64_t *gidx,
                          const int64_t *off, int32_t storage, int32_t grad_bf16,
-                         float *const *p, const void *const *g, int8_t *m_codes,
-                         uint8_t *v_codes, float *m_scale, float *v_scale,
-                         uint16_t *m_bf16, uint16_t *v_bf16, float *m_f32, float *v_f32,
+                         float *const *p, const void *const *g, const orc_ptrs *state,
                          float lr, float beta1, float beta2, float eps, float wd, float pct,
                          int64_t t, int32_t decoupled, int32_t stochastic, int32_t use_pct,
-                         int32_t static_scales, uint64_t seed)
+                         int32_t static_scales, int32_t amsgrad, uint64_t seed)
 {
     if (n_blocks < 0 || t < 1 || storage < ORC_F32 || storage > ORC_Q8_V_ONLY)
         return -1;
-    if (!(pct >= 0.0f && pct <= 100.0f))
+    if (!(pct >= 0.0f && pct <= 100.0f) || !state || !has_buffers(state, storage, amsgrad))
         return -1;
     const orc_hparams h = {lr, beta1, beta2, eps, wd, pct, t, decoupled, stochastic, use_pct,
-                           static_scales, seed};
+                           static_scales, amsgrad, seed};
     float s[5];
     orc_host_scalars(lr, beta1, beta2, wd, t, decoupled, s);
     for (int64_t i = 0; i < n_blocks; i++) {
-        const int64_t o = off[i];
+        const orc_ptrs q = advance(state, off[i], i);
         step_block(p[i], grad_bf16 ? NULL : (const float *)g[i],
                    grad_bf16 ? (const uint16_t *)g[i] : NULL, n[i], gidx[i], storage,
-                   &h, s, m_codes ? m_codes + o : NULL, v_codes ? v_codes + o : NULL,
-                   m_scale ? m_scale + i : NULL, v_scale ? v_scale + i : NULL,
-                   m_bf16 ? m_bf16 + o : NULL, v_bf16 ? v_bf16 + o : NULL,
-                   m_f32 ? m_f32 + o : NULL, v_f32 ? v_f32 + o : NULL, NULL, NULL);
+                   &h, s, &q, NULL, NULL, NULL);
     }
     return 0;
 }
