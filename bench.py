@@ -14,6 +14,7 @@ FETCH_SIZE / WRITE_SIZE counters when a committed counter summary matches
 the current kernel source) and the CPU oracle timed on a bounded sample.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -30,9 +31,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 # algorithmic bytes per parameter (read + write) and per block (scales)
 #   params 4+4, grads 4 (fp32) or 2 (bf16), moments read+write, scales 4+4 per
-#   block per quantized moment
+#   block per quantized moment; AMSGrad adds the running maximum of v, stored
+#   as v is (bf16: 2+2 per parameter; 8-bit: 1+1 and a scale)
 _MOMENT_BYTES = {"bf16": 8, "q8": 4, "q8_v_only": 10}
 _SCALE_BYTES = {"bf16": 0, "q8": 16, "q8_v_only": 8}
+_VMAX_BYTES = {"bf16": (4, 0), "q8": (2, 8), "q8_v_only": (2, 8)}
 
 
 def algorithmic_bytes(cfg):
@@ -40,7 +43,12 @@ def algorithmic_bytes(cfg):
     n = sum(numels)
     blocks = sum(-(-k // 2048) for k in numels)
     g = 2 if cfg.grad_dtype == "bf16" else 4
-    return n * (8 + g + _MOMENT_BYTES[cfg.storage]) + blocks * _SCALE_BYTES[cfg.storage]
+    per_n = 8 + g + _MOMENT_BYTES[cfg.storage]
+    per_b = _SCALE_BYTES[cfg.storage]
+    if cfg.amsgrad:
+        per_n += _VMAX_BYTES[cfg.storage][0]
+        per_b += _VMAX_BYTES[cfg.storage][1]
+    return n * per_n + blocks * per_b
 
 
 def kernel_source_hash():
@@ -74,7 +82,8 @@ def cpu_baseline(cfg, hp, steps=1):
     import workloads
     numels = cfg.numels()
     params = workloads.host_params(cfg.cfg_id, numels)
-    st = oracle.OracleState(numels, cfg.storage, grad_bf16=(cfg.grad_dtype == "bf16"))
+    st = oracle.OracleState(numels, cfg.storage, grad_bf16=(cfg.grad_dtype == "bf16"),
+                            amsgrad=cfg.amsgrad)
     elapsed = 0.0
     for t in range(1, steps + 1):
         grads = workloads.host_grads(cfg.cfg_id, numels, t, dist=cfg.grad_dist,
@@ -100,6 +109,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--static-scales", action="store_true",
                     help="8-bit sets: keep each block's scale once set")
+    ap.add_argument("--amsgrad", action="store_true",
+                    help="keep the running maximum of v (AMSGrad)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's device copy of 4 GiB (counter calibration run)")
     args = ap.parse_args()
@@ -125,6 +136,8 @@ def main():
         return
 
     cfg = workloads.CONFIGS[args.config]
+    if args.amsgrad:
+        cfg = dataclasses.replace(cfg, amsgrad=True)
     numels = cfg.numels()
     n_params = sum(numels)
     params = workloads.device_params(cfg.cfg_id, numels)
@@ -132,7 +145,7 @@ def main():
     for i in range(max(1, args.grad_buffers)):
         gsets.append(workloads.device_grads(cfg.cfg_id, numels, i + 1, dist=cfg.grad_dist,
                                             dtype=cfg.grad_dtype))
-    st = ma.adam_state_create(numels, cfg.storage, cfg.grad_dtype)
+    st = ma.adam_state_create(numels, cfg.storage, cfg.grad_dtype, amsgrad=cfg.amsgrad)
     stream = torch.cuda.current_stream()
     hp = dict(cfg.hp)
     if args.static_scales:
@@ -160,8 +173,9 @@ def main():
 
     alg = algorithmic_bytes(cfg)
     achieved = alg / sec / 1e9
-    # counter readings are taken per workload for the dynamic-scale kernel
-    traffic = None if args.static_scales else traffic_for(cfg.name)
+    # counter readings are taken per workload for the dynamic-scale,
+    # plain-Adam kernel
+    traffic = None if (args.static_scales or cfg.amsgrad) else traffic_for(cfg.name)
     out = {
         "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",
         "value": round(n_params / sec / 1e9, 3),
@@ -186,6 +200,7 @@ def main():
             "stochastic_rounding": bool(hp.get("stochastic")),
             "percentile": hp.get("percentile"),
             "static_scales": bool(hp.get("static_scales")),
+            "amsgrad": cfg.amsgrad,
             "block_size": 2048,
         },
         "roofline": {

@@ -18,13 +18,17 @@
  *     half-size bf16 buffers updated by one fused Adam/AdamW kernel; the
  *     optimizer configuration that a compiled step was set up with is checked
  *     on every step so that a changed moment-storage flag is not missed
- *     (review comment on the drift-detection tuple).
+ *     (review comment on the drift-detection tuple).  The same page names
+ *     AMSGrad as a variant still lacking a fused kernel; it is built here
+ *     (layout option ADAM_OPT_AMSGRAD) after Reddi, Kale & Kumar, "On the
+ *     Convergence of Adam and Beyond" (ICLR 2018), in PyTorch's convention.
  *
  * Numerics of one element (fp32, each operation rounded once; g widened
  * exactly from bf16 when grads are bf16):
  *   [Adam, L2-coupled:  g = fma(wd, p, g)]
  *   m = fma(beta1, m_old, (1-beta1)*g)
  *   v = fma(beta2, v_old, (1-beta2)*(g*g))
+ *   [AMSGrad: w = max(w_old, v), the running maximum; w replaces v below]
  *   p = fma(-lr/(1-beta1^t), m / fma(sqrt(v), 1/sqrt(1-beta2^t), eps), p*decay)
  * with decay = 1 - lr*wd for AdamW and 1 for Adam, the bias-correction
  * scalars formed in fp64 on the host and rounded once to fp32.  bf16
@@ -35,8 +39,11 @@
  * never produced) or 255 (v, uint8); encoding rounds |x| * fl(qmax/A) to
  * nearest-even (or stochastically: up iff u < frac with u a 16-bit draw of
  * Philox4x32-10, key = seed, counter = (flat index / 4, t), word = flat
- * index mod 4, low half for m and high half for v) and pins |x| >= A to
- * qmax; a block with A < 2^-112 stores zero codes and scale 0.
+ * index mod 4, low half for m and high half for v; the AMSGrad maximum
+ * takes the low half of the word at counter (flat index / 4 + 2^63, t)) and
+ * pins |x| >= A to qmax; a block with A < 2^-112 stores zero codes and
+ * scale 0.  The AMSGrad maximum is stored as v is: bf16, or uint8 codes
+ * with their own per-block scale.
  *
  * State layout (device memory owned by the library): tensor k's segment has
  * pad16(numel_k) entries and starts at the sum of the earlier segments (its
@@ -99,7 +106,14 @@ enum adam_buffer {
     ADAM_BUF_V_SCALE = 3, /* float[blocks]             (Q8, Q8_V_ONLY) */
     ADAM_BUF_M_BF16 = 4,  /* uint16[padded elements]   (BF16) */
     ADAM_BUF_V_BF16 = 5,  /* uint16[padded elements]   (BF16) */
-    ADAM_BUF_M_F32 = 6    /* float[padded elements]    (Q8_V_ONLY) */
+    ADAM_BUF_M_F32 = 6,   /* float[padded elements]    (Q8_V_ONLY) */
+    ADAM_BUF_VMAX_CODES = 7, /* uint8[padded elements] (Q8, Q8_V_ONLY with AMSGRAD) */
+    ADAM_BUF_VMAX_SCALE = 8, /* float[blocks]          (Q8, Q8_V_ONLY with AMSGRAD) */
+    ADAM_BUF_VMAX_BF16 = 9   /* uint16[padded elements] (BF16 with AMSGRAD) */
+};
+
+enum adam_options {
+    ADAM_OPT_AMSGRAD = 1u /* keep the running maximum of v (AMSGrad) */
 };
 
 #define ADAM_BLOCK_SIZE 2048 /* the only block size the gfx950 kernels take */
@@ -108,6 +122,7 @@ typedef struct {
     int32_t storage;    /* enum adam_storage */
     int32_t grad_dtype; /* enum adam_grad_dtype */
     int32_t block_size; /* must be ADAM_BLOCK_SIZE */
+    uint32_t options;   /* enum adam_options bits; unknown bits are EINVAL */
 } adam_layout;
 
 typedef struct {
@@ -126,7 +141,8 @@ typedef struct {
 /*
  * Bytes of optimizer state for a tensor list, without allocating:
  *   sum_k pad16(numel_k) * e + blocks * s, with (e, s) = (4, 0) for BF16,
- *   (2, 8) for Q8 and (5, 4) for Q8_V_ONLY.
+ *   (2, 8) for Q8 and (5, 4) for Q8_V_ONLY; ADAM_OPT_AMSGRAD adds (2, 0)
+ *   for BF16 and (1, 4) for the 8-bit modes.
  * The per-block descriptor table (16 bytes per block) and the per-tensor
  * pointer table (16 bytes per tensor) are bookkeeping, not counted.
  * Memory accounting follows the 8-bit Adam page (GetMemoryUsage).
@@ -190,12 +206,12 @@ int adam_state_write(adam_state *s, int32_t which, const void *src, int64_t nbyt
  * marker per moment so that a reader never assumes a buffer the writer did
  * not store.  The serialized form is a self-describing little-endian byte
  * stream in host memory:
- *   header   "MEAMSTAT", u32 version (1), u32 header bytes (32 + 8*n),
- *            i32 storage, i32 grad_dtype, i32 block_size, i32 n_tensors,
- *            i64 numels[n_tensors]
- *   records  one per state buffer the storage mode has (enum adam_buffer
- *            order): u32 buffer id, u32 0, u64 byte count, the bytes, zero
- *            padding to a multiple of 8
+ *   header   "MEAMSTAT", u32 version (2), u32 header bytes (40 + 8*n),
+ *            i32 storage, i32 grad_dtype, i32 block_size, u32 options,
+ *            i32 n_tensors, u32 0, i64 numels[n_tensors]
+ *   records  one per state buffer the layout has (enum adam_buffer order):
+ *            u32 buffer id, u32 0, u64 byte count, the bytes, zero padding
+ *            to a multiple of 8
  *   trailer  u32 0xFFFFFFFF, u32 record count, u64 checksum (a 64-bit
  *            multiply-xor hash over every preceding byte, 8 bytes at a time)
  * adam_state_serialized_bytes: the stream's size for this state (< 0 on a

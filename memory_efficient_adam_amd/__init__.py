@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     AdamState,
     BUFFERS,
     GRAD_DTYPES,
+    OPT_AMSGRAD,
     STORAGES,
     adam_last_error,
     adam_state_buffer_bytes,

@@ -9,7 +9,8 @@ ADAM_BLOCK_SIZE = 2048
 STORAGES = {"bf16": 1, "q8": 2, "q8_v_only": 3}
 GRAD_DTYPES = {"f32": 0, "bf16": 1}
 BUFFERS = {"m_codes": 0, "v_codes": 1, "m_scale": 2, "v_scale": 3, "m_bf16": 4,
-           "v_bf16": 5, "m_f32": 6}
+           "v_bf16": 5, "m_f32": 6, "vmax_codes": 7, "vmax_scale": 8, "vmax_bf16": 9}
+OPT_AMSGRAD = 1
 _F_DECOUPLED, _F_STOCHASTIC, _F_PERCENTILE, _F_STATIC_SCALES = 1, 2, 4, 8
 _STATUS = {0: "ADAM_OK", -1: "ADAM_EINVAL", -2: "ADAM_EMODE", -3: "ADAM_EALIGN",
            -4: "ADAM_ENOMEM", -5: "ADAM_EDEVICE"}
@@ -17,7 +18,7 @@ _STATUS = {0: "ADAM_OK", -1: "ADAM_EINVAL", -2: "ADAM_EMODE", -3: "ADAM_EALIGN",
 
 class adam_layout(ctypes.Structure):
     _fields_ = [("storage", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
-                ("block_size", ctypes.c_int32)]
+                ("block_size", ctypes.c_int32), ("options", ctypes.c_uint32)]
 
 
 class adam_hparams(ctypes.Structure):
@@ -90,10 +91,10 @@ def _check(rc):
         raise AdamError(rc, adam_last_error())
 
 
-def _layout(storage, grad_dtype, block_size=ADAM_BLOCK_SIZE):
+def _layout(storage, grad_dtype, block_size=ADAM_BLOCK_SIZE, options=0):
     return adam_layout(STORAGES.get(storage, storage) if isinstance(storage, str) else storage,
                        GRAD_DTYPES.get(grad_dtype, grad_dtype) if isinstance(grad_dtype, str)
-                       else grad_dtype, block_size)
+                       else grad_dtype, block_size, options)
 
 
 def _numels(numels):
@@ -110,9 +111,10 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def adam_state_bytes(numels, storage, grad_dtype="f32", block_size=ADAM_BLOCK_SIZE):
+def adam_state_bytes(numels, storage, grad_dtype="f32", block_size=ADAM_BLOCK_SIZE,
+                     amsgrad=False):
     n, arr = _numels(numels)
-    lay = _layout(storage, grad_dtype, block_size)
+    lay = _layout(storage, grad_dtype, block_size, OPT_AMSGRAD if amsgrad else 0)
     rc = library().adam_state_bytes(n, arr, ctypes.byref(lay))
     if rc < 0:
         raise AdamError(int(rc), adam_last_error())
@@ -139,11 +141,17 @@ class AdamState:
     def storage(self):
         return {v: k for k, v in STORAGES.items()}[self.layout.storage]
 
+    @property
+    def amsgrad(self):
+        return bool(self.layout.options & OPT_AMSGRAD)
+
 
 def adam_state_create(numels, storage, grad_dtype="f32", block_size=ADAM_BLOCK_SIZE,
-                      stream=None):
+                      amsgrad=False, stream=None):
+    """A zero state for tensors of the given sizes; amsgrad keeps the running
+    maximum of v (layout option ADAM_OPT_AMSGRAD)."""
     n, arr = _numels(numels)
-    lay = _layout(storage, grad_dtype, block_size)
+    lay = _layout(storage, grad_dtype, block_size, OPT_AMSGRAD if amsgrad else 0)
     h = ctypes.c_void_p()
     _check(library().adam_state_create(ctypes.byref(h), n, arr, ctypes.byref(lay),
                                        _stream(stream)))
@@ -160,8 +168,8 @@ def adam_step(state, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
     """One step over all tensors.  params: fp32 device tensors (updated in
     place); grads: fp32 or bf16 device tensors; percentile=None selects the
     absmax block statistic; static_scales keeps each block's scale once set.
-    expect: (storage, grad_dtype[, block_size]) the caller believes the state
-    has (default: the state's own layout)."""
+    expect: (storage, grad_dtype[, block_size[, options]]) the caller believes
+    the state has (default: the state's own layout)."""
     n = len(state.numels)
     if len(params) != n or len(grads) != n:
         raise ValueError(f"expected {n} params and grads")
@@ -187,7 +195,8 @@ def adam_state_buffer_bytes(state, which):
 
 
 _BUF_DTYPES = {"m_codes": "int8", "v_codes": "uint8", "m_scale": "float32",
-               "v_scale": "float32", "m_bf16": "int16", "v_bf16": "int16", "m_f32": "float32"}
+               "v_scale": "float32", "m_bf16": "int16", "v_bf16": "int16", "m_f32": "float32",
+               "vmax_codes": "uint8", "vmax_scale": "float32", "vmax_bf16": "int16"}
 
 
 def adam_state_read(state, which, out=None, stream=None):

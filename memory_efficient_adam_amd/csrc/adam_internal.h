@@ -42,6 +42,8 @@ struct StepArgs {
     void *v_state;   // bf16 / uint8 codes
     float *m_scale;  // per block (Q8)
     float *v_scale;  // per block (Q8, Q8_V_ONLY)
+    void *w_state;   // AMSGrad running max of v: bf16 / uint8 codes (else NULL)
+    float *w_scale;  // its per-block scale (8-bit storage with AMSGrad)
     float step;      // lr / (1 - beta1^t)
     float ibc2;      // 1 / sqrt(1 - beta2^t)
     float decay;     // 1 - lr*wd (AdamW) or 1 (Adam)
@@ -61,6 +63,7 @@ struct Variant {
     bool stochastic;
     bool percentile;
     bool static_scales;  // keep a block's scale once set (8-bit storage)
+    bool amsgrad;        // the state holds the running max of v
 };
 
 // Enqueues the step kernel over every descriptor.

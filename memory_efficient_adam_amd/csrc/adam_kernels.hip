@@ -140,23 +140,23 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     return v;
 }
 
-// Block-wide max of two non-negative values (one barrier).
-__device__ __forceinline__ void block_max2(float &a, float &b, float (*red)[kWaves]) {
+// Block-wide max of N non-negative values per thread (one barrier).
+template <int N>
+__device__ __forceinline__ void block_max(float (&x)[N], float (*red)[kWaves]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    a = wave_max(a);
-    b = wave_max(b);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = wave_max(x[i]);
     if (kWaves == 1) return;
     if (lane == 0) {
-        red[0][wave] = a;
-        red[1][wave] = b;
+#pragma unroll
+        for (int i = 0; i < N; ++i) red[i][wave] = x[i];
     }
     __syncthreads();
-    a = red[0][0];
-    b = red[1][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-        a = fmaxf(a, red[0][w]);
-        b = fmaxf(b, red[1][w]);
+    for (int i = 0; i < N; ++i) {
+        x[i] = red[i][0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) x[i] = fmaxf(x[i], red[i][w]);
     }
 }
 
@@ -263,14 +263,16 @@ __device__ __forceinline__ BlockCtx load_ctx(const StepArgs &a, uint32_t idx) {
     return c;
 }
 
-// Raw (undecoded) per-thread data of one block, as loaded.
-template <int kStore, bool kGradBf16>
+// Raw (undecoded) per-thread data of one block, as loaded.  w: the AMSGrad
+// running maximum of v, stored as v is (unused without kAms).
+template <int kStore, bool kGradBf16, bool kAms>
 struct BlockRegs {
     float p[kItems];
     uint32_t g[kGradBf16 ? kItems / 2 : kItems];  // fp32 bits, or bf16 pairs
     uint32_t m[kStore == kStoreBf16 ? kItems / 2 : (kStore == kStoreQ8 ? kGroups : kItems)];
     uint32_t v[kStore == kStoreBf16 ? kItems / 2 : kGroups];
-    float Am, Av;  // stored scales of the 8-bit moments
+    uint32_t w[!kAms ? 1 : (kStore == kStoreBf16 ? kItems / 2 : kGroups)];
+    float Am, Av, Aw;  // stored scales of the 8-bit moments
 };
 
 // Issues every load of one block.  kFull: the block has 2048 live elements,
@@ -278,12 +280,13 @@ struct BlockRegs {
 // compiler's wait counts then let the loads stay in flight across the
 // previous block's compute).  Otherwise the ragged last group uses element
 // loads and state slots past the tensor's padded segment are not touched.
-template <int kStore, bool kGradBf16, bool kFull>
+template <int kStore, bool kGradBf16, bool kAms, bool kFull>
 __device__ __forceinline__ void load_data(const StepArgs &a, const BlockCtx &c,
-                                          BlockRegs<kStore, kGradBf16> &r) {
+                                          BlockRegs<kStore, kGradBf16, kAms> &r) {
     const int tid = threadIdx.x;
     r.Am = kStore == kStoreQ8 ? a.m_scale[c.slot] : 0.0f;
     r.Av = kStore != kStoreBf16 ? a.v_scale[c.slot] : 0.0f;
+    r.Aw = kAms && kStore != kStoreBf16 ? a.w_scale[c.slot] : 0.0f;
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
         const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
@@ -325,8 +328,14 @@ __device__ __forceinline__ void load_data(const StepArgs &a, const BlockCtx &c,
             }
             r.m[2 * j] = hm.x; r.m[2 * j + 1] = hm.y;
             r.v[2 * j] = hv.x; r.v[2 * j + 1] = hv.y;
+            if constexpr (kAms) {
+                u32x2 hw = {0u, 0u};
+                if (in) hw = ld_u32x2(reinterpret_cast<const uint16_t *>(a.w_state) + s);
+                r.w[2 * j] = hw.x; r.w[2 * j + 1] = hw.y;
+            }
         } else {
             r.v[j] = in ? ld_u32(reinterpret_cast<const uint8_t *>(a.v_state) + s) : 0u;
+            if constexpr (kAms) r.w[j] = in ? ld_u32(reinterpret_cast<const uint8_t *>(a.w_state) + s) : 0u;
             if constexpr (kStore == kStoreQ8) {
                 r.m[j] = in ? ld_u32(reinterpret_cast<const int8_t *>(a.m_state) + s) : 0u;
             } else {
@@ -339,9 +348,9 @@ __device__ __forceinline__ void load_data(const StepArgs &a, const BlockCtx &c,
     }
 }
 
-// LDS of one block's max reduction.
+// LDS of one block's max reduction (m, v and the AMSGrad maximum).
 struct BlockLds {
-    float red[2][kWaves];
+    float red[3][kWaves];
 };
 
 // LDS of the percentile statistic (radix-select histogram + scan scratch).
@@ -358,16 +367,43 @@ struct SelectLds<true> {
     __device__ uint32_t *scratch() { return s; }
 };
 
+// Codes of four unsigned values x[b..b+3] (v, or the AMSGrad maximum) packed
+// into the bytes of one word; u: the group's four Philox words, of which the
+// 16 bits at `shift` are the draws.
+template <bool kSR>
+__device__ __forceinline__ uint32_t pack_u8(const float (&x)[kItems], int b, float pin, float r,
+                                            const uint32_t (&u)[4], int shift) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float ax = fabsf(x[b + k]);
+        if constexpr (kSR) {
+            c |= code_magnitude<true, true>(ax, pin, r, 255u, (u[k] >> shift) & 0xFFFFu) << (8 * k);
+        } else {
+            // nearest-even rounding, clamped to [0, 255], packed into byte k: the
+            // clamp is the end pin (|x| >= A gives y >= 254.99998)
+            c = __builtin_amdgcn_cvt_pk_u8_f32(ax * r, k, c);
+        }
+    }
+    return c;
+}
+
+__device__ __forceinline__ float uniform(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 // Decode, update, store params; block statistic; requantize and store state.
 // kStatic: a moment whose stored scale is already set (>= kTiny) keeps it and
 // skips its statistic; values at or beyond it saturate through the end pin.
-template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kFull>
+// kAms: AMSGrad -- the running maximum w of v is decoded, updated to
+// max(w, v), used in the denominator and stored as v is, with its own scale.
+template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kAms, bool kFull>
 __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx &c,
-                                              const BlockRegs<kStore, kGradBf16> &r, BlockLds &lds,
-                                              SelectLds<kPct> &sel) {
+                                              const BlockRegs<kStore, kGradBf16, kAms> &r,
+                                              BlockLds &lds, SelectLds<kPct> &sel) {
     constexpr bool kQuantM = (kStore == kStoreQ8);
     const int tid = threadIdx.x;
-    float p[kItems], g[kItems], mo[kItems], vo[kItems];
+    float p[kItems], g[kItems], mo[kItems], vo[kItems], wo[kAms ? kItems : 1];
 
     // ---- decode
     constexpr float Rm = 1.0f / 127.0f;
@@ -380,8 +416,10 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         if constexpr (kStore == kStoreBf16) {
             mo[i] = bf16_to_f32((r.m[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
             vo[i] = bf16_to_f32((r.v[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
+            if constexpr (kAms) wo[i] = bf16_to_f32((r.w[i / 2] >> (16 * (i & 1))) & 0xFFFFu);
         } else {
             vo[i] = ((float)((r.v[i / 4] >> (8 * (i & 3))) & 0xFFu) * Rv) * r.Av;
+            if constexpr (kAms) wo[i] = ((float)((r.w[i / 4] >> (8 * (i & 3))) & 0xFFu) * Rv) * r.Aw;
             if constexpr (kQuantM) {
                 const int32_t q = ((int32_t)(r.m[i / 4] << (24 - 8 * (i & 3)))) >> 24;
                 mo[i] = ((float)q * Rm) * r.Am;
@@ -396,13 +434,19 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 #pragma unroll
         for (int i = 0; i < kItems; ++i) g[i] = fmaf(a.wd, p[i], g[i]);
     }
-    float mmax = 0.0f, vmax = 0.0f;
+    float mmax = 0.0f, vmax = 0.0f, wmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const float gi = g[i];
         const float m = fmaf(a.beta1, mo[i], a.omb1 * gi);
         const float v = fmaf(a.beta2, vo[i], a.omb2 * (gi * gi));
-        const float den = fmaf(sqrtf(v), a.ibc2, a.eps);
+        float vd = v;  // the second moment the denominator uses
+        if constexpr (kAms) {
+            vd = fmaxf(wo[i], v);
+            wo[i] = vd;
+            wmax = fmaxf(wmax, vd);
+        }
+        const float den = fmaf(sqrtf(vd), a.ibc2, a.eps);
         p[i] = fmaf(-a.step, m / den, p[i] * a.decay);
         mo[i] = m;
         vo[i] = v;
@@ -435,24 +479,43 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                                   f32_to_bf16(vo[4 * j + 2]) | (f32_to_bf16(vo[4 * j + 3]) << 16)};
                 st_u32x2(reinterpret_cast<uint16_t *>(a.m_state) + s, hm);
                 st_u32x2(reinterpret_cast<uint16_t *>(a.v_state) + s, hv);
+                if constexpr (kAms) {
+                    const u32x2 hw = {f32_to_bf16(wo[4 * j]) | (f32_to_bf16(wo[4 * j + 1]) << 16),
+                                      f32_to_bf16(wo[4 * j + 2]) | (f32_to_bf16(wo[4 * j + 3]) << 16)};
+                    st_u32x2(reinterpret_cast<uint16_t *>(a.w_state) + s, hw);
+                }
             }
         }
     } else {
         // ---- block statistic (the old scales are block-uniform: every lane
         // read the same word, so readfirstlane makes the branches scalar)
-        bool keep_m = false, keep_v = false;
-        float Am_old = 0.0f, Av_old = 0.0f;
+        bool keep_m = false, keep_v = false, keep_w = false;
+        float Am_old = 0.0f, Av_old = 0.0f, Aw_old = 0.0f;
         if constexpr (kStatic) {
-            Av_old = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, r.Av)));
+            Av_old = uniform(r.Av);
             keep_v = Av_old >= kTiny;
             if constexpr (kQuantM) {
-                Am_old = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, r.Am)));
+                Am_old = uniform(r.Am);
                 keep_m = Am_old >= kTiny;
             }
+            if constexpr (kAms) {
+                Aw_old = uniform(r.Aw);
+                keep_w = Aw_old >= kTiny;
+            }
         }
-        const bool need_m = kQuantM && !keep_m, need_v = !keep_v;
-        if (need_m || need_v) block_max2(mmax, vmax, lds.red);
-        float Amn = keep_m ? Am_old : mmax, Avn = keep_v ? Av_old : vmax;
+        const bool need_m = kQuantM && !keep_m, need_v = !keep_v, need_w = kAms && !keep_w;
+        if (need_m || need_v || need_w) {
+            if constexpr (kAms) {
+                float x[3] = {mmax, vmax, wmax};
+                block_max<3>(x, lds.red);
+                mmax = x[0]; vmax = x[1]; wmax = x[2];
+            } else {
+                float x[2] = {mmax, vmax};
+                block_max<2>(x, lds.red);
+                mmax = x[0]; vmax = x[1];
+            }
+        }
+        float Amn = keep_m ? Am_old : mmax, Avn = keep_v ? Av_old : vmax, Awn = keep_w ? Aw_old : wmax;
         if constexpr (kPct) {
             const uint32_t rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
             uint32_t key[kItems];
@@ -468,15 +531,25 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                 const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
                 Avn = sv < kTiny ? vmax : sv;
             }
+            if constexpr (kAms) {
+                if (need_w) {
+#pragma unroll
+                    for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(wo[i]) & 0x7FFFFFFFu;
+                    const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
+                    Awn = sv < kTiny ? wmax : sv;
+                }
+            }
         }
         constexpr bool kPin = kSR || kPct || kStatic;
-        const bool mzero = !(Amn >= kTiny), vzero = !(Avn >= kTiny);
+        const bool mzero = !(Amn >= kTiny), vzero = !(Avn >= kTiny), wzero = !(Awn >= kTiny);
         const float rm = mzero ? 0.0f : 127.0f / Amn;
         const float rv = vzero ? 0.0f : 255.0f / Avn;
+        const float rw = (!kAms || wzero) ? 0.0f : 255.0f / Awn;
         // a zero block has r = 0, so y = 0 and every code is 0; its pin
         // threshold is +inf so that the end pin never fires
         const float pin_m = mzero ? __builtin_inff() : Amn;
         const float pin_v = vzero ? __builtin_inff() : Avn;
+        const float pin_w = wzero ? __builtin_inff() : Awn;
 
         // ---- requantize and store codes
 #pragma unroll
@@ -484,33 +557,28 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
             if (!kFull && e0 >= c.npad) continue;
             const size_t s = c.gidx + e0;
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
+            uint32_t rnd[4] = {0u, 0u, 0u, 0u}, rnd_w[4] = {0u, 0u, 0u, 0u};
             if constexpr (kSR) {
                 const uint64_t grp = s >> 2;
                 uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), a.t_lo, a.t_hi};
                 philox4x32_10(ctr, a.seed_lo, a.seed_hi);
-                w[0] = ctr[0]; w[1] = ctr[1]; w[2] = ctr[2]; w[3] = ctr[3];
-            }
-            uint32_t cv = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float av = fabsf(vo[4 * j + k]);
-                if constexpr (kSR) {
-                    const uint32_t q = code_magnitude<true, true>(av, pin_v, rv, 255u, w[k] >> 16);
-                    cv |= q << (8 * k);
-                } else {
-                    // nearest-even rounding, clamped to [0, 255], packed into byte k: the
-                    // clamp is the end pin (|v| >= A gives y >= 254.99998)
-                    cv = __builtin_amdgcn_cvt_pk_u8_f32(av * rv, k, cv);
+                rnd[0] = ctr[0]; rnd[1] = ctr[1]; rnd[2] = ctr[2]; rnd[3] = ctr[3];
+                if constexpr (kAms) {
+                    // the maximum's draws: the counter stream with bit 63 set
+                    uint32_t ctr_w[4] = {(uint32_t)grp, (uint32_t)(grp >> 32) | 0x80000000u, a.t_lo, a.t_hi};
+                    philox4x32_10(ctr_w, a.seed_lo, a.seed_hi);
+                    rnd_w[0] = ctr_w[0]; rnd_w[1] = ctr_w[1]; rnd_w[2] = ctr_w[2]; rnd_w[3] = ctr_w[3];
                 }
             }
-            st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s, cv);
+            st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s, pack_u8<kSR>(vo, 4 * j, pin_v, rv, rnd, 16));
+            if constexpr (kAms)
+                st_u32(reinterpret_cast<uint8_t *>(a.w_state) + s, pack_u8<kSR>(wo, 4 * j, pin_w, rw, rnd_w, 0));
             if constexpr (kQuantM) {
                 uint32_t cm = 0;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const float x = mo[4 * j + k];
-                    const uint32_t q = code_magnitude<kSR, kPin>(fabsf(x), pin_m, rm, 127u, w[k] & 0xFFFFu);
+                    const uint32_t q = code_magnitude<kSR, kPin>(fabsf(x), pin_m, rm, 127u, rnd[k] & 0xFFFFu);
                     const uint32_t qs = x < 0.0f ? 0u - q : q;  // -0 gives 0
                     cm |= (qs & 0xFFu) << (8 * k);
                 }
@@ -525,6 +593,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         if (tid == 0) {
             if (need_m) a.m_scale[c.slot] = mzero ? 0.0f : Amn;
             if (need_v) a.v_scale[c.slot] = vzero ? 0.0f : Avn;
+            if (need_w) a.w_scale[c.slot] = wzero ? 0.0f : Awn;
         }
     }
 }
@@ -533,19 +602,19 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 // One workgroup per block; workgroups beyond the grid limit loop (stride =
 // grid size).  Descriptors [0, n_full) are full blocks, whose path has no
 // tail checks; the rest are the tensors' ragged last blocks.
-template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic>
+template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kAms>
 __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
     __shared__ BlockLds lds;
     __shared__ SelectLds<kPct> sel;
     for (uint32_t i = blockIdx.x; i < a.n_all; i += gridDim.x) {
-        BlockRegs<kStore, kGradBf16> r;
+        BlockRegs<kStore, kGradBf16, kAms> r;
         const BlockCtx c = load_ctx<kGradBf16>(a, i);
         if (i < a.n_full) {
-            load_data<kStore, kGradBf16, true>(a, c, r);
-            process_block<kStore, kGradBf16, kSR, kPct, kStatic, true>(a, c, r, lds, sel);
+            load_data<kStore, kGradBf16, kAms, true>(a, c, r);
+            process_block<kStore, kGradBf16, kSR, kPct, kStatic, kAms, true>(a, c, r, lds, sel);
         } else {
-            load_data<kStore, kGradBf16, false>(a, c, r);
-            process_block<kStore, kGradBf16, kSR, kPct, kStatic, false>(a, c, r, lds, sel);
+            load_data<kStore, kGradBf16, kAms, false>(a, c, r);
+            process_block<kStore, kGradBf16, kSR, kPct, kStatic, kAms, false>(a, c, r, lds, sel);
         }
         if (i + gridDim.x < a.n_all) __syncthreads();  // LDS reused by the next block
     }
@@ -567,49 +636,54 @@ constexpr int kCuLdsBytes = 160 * 1024;
 constexpr size_t reserve_lds(int resident) { return resident >= 8 ? 0 : kCuLdsBytes / (resident + 1) + 1024; }
 constexpr uint32_t kMaxGrid = (1u << 24) - 1;  // grid.x * 256 work-items < 2^32
 
-template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic = false>
+template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kAms>
 hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     const uint32_t grid = std::min<uint32_t>(a.n_all, kMaxGrid);
     if (grid == 0) return hipSuccess;
     constexpr int kResident = kStore == kStoreBf16 ? ADAM_BF16_RESIDENT_PER_CU : ADAM_Q8_RESIDENT_PER_CU;
     constexpr size_t kStaticLds = sizeof(BlockLds) + sizeof(SelectLds<kPct>);
     constexpr size_t kDyn = reserve_lds(kResident) > kStaticLds ? reserve_lds(kResident) - kStaticLds : 0;
-    hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct, kStatic>), dim3(grid), dim3(kThreads), kDyn,
-                       stream, a);
+    hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct, kStatic, kAms>), dim3(grid), dim3(kThreads),
+                       kDyn, stream, a);
     return hipGetLastError();
 }
 
-template <int kStore, bool kGradBf16, bool kStatic>
+template <int kStore, bool kGradBf16, bool kStatic, bool kAms>
 hipError_t launch_rounding(const Variant &v, const StepArgs &a, hipStream_t stream) {
     if (v.stochastic)
-        return v.percentile ? launch_one<kStore, kGradBf16, true, true, kStatic>(a, stream)
-                            : launch_one<kStore, kGradBf16, true, false, kStatic>(a, stream);
-    return v.percentile ? launch_one<kStore, kGradBf16, false, true, kStatic>(a, stream)
-                        : launch_one<kStore, kGradBf16, false, false, kStatic>(a, stream);
+        return v.percentile ? launch_one<kStore, kGradBf16, true, true, kStatic, kAms>(a, stream)
+                            : launch_one<kStore, kGradBf16, true, false, kStatic, kAms>(a, stream);
+    return v.percentile ? launch_one<kStore, kGradBf16, false, true, kStatic, kAms>(a, stream)
+                        : launch_one<kStore, kGradBf16, false, false, kStatic, kAms>(a, stream);
 }
 
-template <int kStore, bool kGradBf16>
+template <int kStore, bool kGradBf16, bool kAms>
 hipError_t launch_q(const Variant &v, const StepArgs &a, hipStream_t stream) {
-    return v.static_scales ? launch_rounding<kStore, kGradBf16, true>(v, a, stream)
-                           : launch_rounding<kStore, kGradBf16, false>(v, a, stream);
+    return v.static_scales ? launch_rounding<kStore, kGradBf16, true, kAms>(v, a, stream)
+                           : launch_rounding<kStore, kGradBf16, false, kAms>(v, a, stream);
+}
+
+template <bool kAms>
+hipError_t launch_storage(const Variant &v, const StepArgs &a, hipStream_t stream) {
+    switch (v.storage) {
+    case kStoreBf16:
+        return v.grad_bf16 ? launch_one<kStoreBf16, true, false, false, false, kAms>(a, stream)
+                           : launch_one<kStoreBf16, false, false, false, false, kAms>(a, stream);
+    case kStoreQ8:
+        return v.grad_bf16 ? launch_q<kStoreQ8, true, kAms>(v, a, stream)
+                           : launch_q<kStoreQ8, false, kAms>(v, a, stream);
+    case kStoreQ8VOnly:
+        return v.grad_bf16 ? launch_q<kStoreQ8VOnly, true, kAms>(v, a, stream)
+                           : launch_q<kStoreQ8VOnly, false, kAms>(v, a, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_step(const Variant &v, const StepArgs &a, hipStream_t stream) {
-    switch (v.storage) {
-    case kStoreBf16:
-        return v.grad_bf16 ? launch_one<kStoreBf16, true, false, false>(a, stream)
-                           : launch_one<kStoreBf16, false, false, false>(a, stream);
-    case kStoreQ8:
-        return v.grad_bf16 ? launch_q<kStoreQ8, true>(v, a, stream)
-                           : launch_q<kStoreQ8, false>(v, a, stream);
-    case kStoreQ8VOnly:
-        return v.grad_bf16 ? launch_q<kStoreQ8VOnly, true>(v, a, stream)
-                           : launch_q<kStoreQ8VOnly, false>(v, a, stream);
-    default:
-        return hipErrorInvalidValue;
-    }
+    return v.amsgrad ? launch_storage<true>(v, a, stream) : launch_storage<false>(v, a, stream);
 }
 
 }  // namespace adam_mi355x

@@ -54,6 +54,8 @@ struct adam_state {
     void *v = nullptr;                   // bf16 / uint8 second moment
     float *m_scale = nullptr;
     float *v_scale = nullptr;
+    void *w = nullptr;                   // AMSGrad running max of v: bf16 / uint8
+    float *w_scale = nullptr;
 };
 
 namespace {
@@ -78,6 +80,7 @@ int check_layout(const adam_layout *l) {
     if (l->block_size != ADAM_BLOCK_SIZE)
         return fail(ADAM_EINVAL, "block_size must be " + std::to_string(ADAM_BLOCK_SIZE) + ", got " +
                                      std::to_string(l->block_size));
+    if (l->options & ~(uint32_t)ADAM_OPT_AMSGRAD) return fail(ADAM_EINVAL, "unknown layout option bits");
     return ADAM_OK;
 }
 
@@ -90,12 +93,18 @@ int check_numels(int32_t n_tensors, const int64_t *numels) {
     return ADAM_OK;
 }
 
-// (bytes per padded element, bytes per block) of each storage mode
-void storage_costs(int32_t storage, int64_t &per_elem, int64_t &per_block) {
-    switch (storage) {
+bool amsgrad(const adam_layout &l) { return (l.options & ADAM_OPT_AMSGRAD) != 0; }
+
+// (bytes per padded element, bytes per block) of a layout's state
+void storage_costs(const adam_layout &l, int64_t &per_elem, int64_t &per_block) {
+    switch (l.storage) {
     case ADAM_STORE_BF16: per_elem = 4; per_block = 0; break;
     case ADAM_STORE_Q8: per_elem = 2; per_block = 8; break;
     default: per_elem = 5; per_block = 4; break;
+    }
+    if (amsgrad(l)) {  // the running maximum is stored as v is
+        per_elem += l.storage == ADAM_STORE_BF16 ? 2 : 1;
+        per_block += l.storage == ADAM_STORE_BF16 ? 0 : 4;
     }
 }
 
@@ -141,6 +150,8 @@ void release(adam_state *s) {
         (void)hipFree(s->v);
         (void)hipFree(s->m_scale);
         (void)hipFree(s->v_scale);
+        (void)hipFree(s->w);
+        (void)hipFree(s->w_scale);
         if (cur >= 0 && cur != s->device) (void)hipSetDevice(cur);
     }
     delete s;
@@ -165,6 +176,7 @@ struct BufferView {
 
 BufferView buffer_of(const adam_state *s, int32_t which) {
     const int32_t st = s->layout.storage;
+    const bool ams = amsgrad(s->layout);
     switch (which) {
     case ADAM_BUF_M_CODES: return st == ADAM_STORE_Q8 ? BufferView{s->m, s->padded} : BufferView{nullptr, -1};
     case ADAM_BUF_V_CODES: return st != ADAM_STORE_BF16 ? BufferView{s->v, s->padded} : BufferView{nullptr, -1};
@@ -176,6 +188,12 @@ BufferView buffer_of(const adam_state *s, int32_t which) {
     case ADAM_BUF_V_BF16: return st == ADAM_STORE_BF16 ? BufferView{s->v, 2 * s->padded} : BufferView{nullptr, -1};
     case ADAM_BUF_M_F32:
         return st == ADAM_STORE_Q8_V_ONLY ? BufferView{s->m, 4 * s->padded} : BufferView{nullptr, -1};
+    case ADAM_BUF_VMAX_CODES:
+        return ams && st != ADAM_STORE_BF16 ? BufferView{s->w, s->padded} : BufferView{nullptr, -1};
+    case ADAM_BUF_VMAX_SCALE:
+        return ams && st != ADAM_STORE_BF16 ? BufferView{s->w_scale, 4 * s->nblocks} : BufferView{nullptr, -1};
+    case ADAM_BUF_VMAX_BF16:
+        return ams && st == ADAM_STORE_BF16 ? BufferView{s->w, 2 * s->padded} : BufferView{nullptr, -1};
     default: return BufferView{nullptr, -1};
     }
 }
@@ -191,7 +209,7 @@ int64_t adam_state_bytes(int32_t n_tensors, const int64_t *numels, const adam_la
     if (rc) return rc;
     if ((rc = check_layout(layout))) return rc;
     int64_t per_elem, per_block;
-    storage_costs(layout->storage, per_elem, per_block);
+    storage_costs(*layout, per_elem, per_block);
     int64_t total = 0;
     for (int32_t k = 0; k < n_tensors; ++k) total += pad16(numels[k]) * per_elem + blocks_of(numels[k]) * per_block;
     return total;
@@ -239,8 +257,6 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
     }
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-    int64_t per_elem, per_block;
-    storage_costs(layout->storage, per_elem, per_block);
     const int32_t st = layout->storage;
     const int64_t m_bytes = st == ADAM_STORE_BF16 ? 2 * s->padded : (st == ADAM_STORE_Q8 ? s->padded : 4 * s->padded);
     const int64_t v_bytes = st == ADAM_STORE_BF16 ? 2 * s->padded : s->padded;
@@ -253,6 +269,12 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
         return rc;
     }
     if (st != ADAM_STORE_BF16 && (rc = alloc_zeroed((void **)&s->v_scale, 4 * s->nblocks, stream))) {
+        release(s);
+        return rc;
+    }
+    if (amsgrad(*layout) &&
+        ((rc = alloc_zeroed(&s->w, st == ADAM_STORE_BF16 ? 2 * s->padded : s->padded, stream)) ||
+         (st != ADAM_STORE_BF16 && (rc = alloc_zeroed((void **)&s->w_scale, 4 * s->nblocks, stream))))) {
         release(s);
         return rc;
     }
@@ -304,7 +326,7 @@ void adam_state_destroy(adam_state *s) { release(s); }
 // ---------------------------------------------------------------- checkpoint
 namespace {
 constexpr char kMagic[8] = {'M', 'E', 'A', 'M', 'S', 'T', 'A', 'T'};
-constexpr uint32_t kFormatVersion = 1;
+constexpr uint32_t kFormatVersion = 2;
 constexpr uint32_t kEndMarker = 0xFFFFFFFFu;
 
 int64_t align8(int64_t n) { return (n + 7) / 8 * 8; }
@@ -324,16 +346,26 @@ uint64_t stream_hash(const uint8_t *p, int64_t n) {
     return h ^ (h >> 32);
 }
 
-// The state buffers a storage mode has, in enum adam_buffer order.
-std::vector<int32_t> buffers_of(int32_t storage) {
-    switch (storage) {
-    case ADAM_STORE_BF16: return {ADAM_BUF_M_BF16, ADAM_BUF_V_BF16};
-    case ADAM_STORE_Q8: return {ADAM_BUF_M_CODES, ADAM_BUF_V_CODES, ADAM_BUF_M_SCALE, ADAM_BUF_V_SCALE};
-    default: return {ADAM_BUF_V_CODES, ADAM_BUF_V_SCALE, ADAM_BUF_M_F32};
+// The state buffers a layout has, in enum adam_buffer order.
+std::vector<int32_t> buffers_of(const adam_layout &l) {
+    std::vector<int32_t> b;
+    switch (l.storage) {
+    case ADAM_STORE_BF16: b = {ADAM_BUF_M_BF16, ADAM_BUF_V_BF16}; break;
+    case ADAM_STORE_Q8: b = {ADAM_BUF_M_CODES, ADAM_BUF_V_CODES, ADAM_BUF_M_SCALE, ADAM_BUF_V_SCALE}; break;
+    default: b = {ADAM_BUF_V_CODES, ADAM_BUF_V_SCALE, ADAM_BUF_M_F32}; break;
     }
+    if (amsgrad(l)) {
+        if (l.storage == ADAM_STORE_BF16) {
+            b.push_back(ADAM_BUF_VMAX_BF16);
+        } else {
+            b.push_back(ADAM_BUF_VMAX_CODES);
+            b.push_back(ADAM_BUF_VMAX_SCALE);
+        }
+    }
+    return b;
 }
 
-int64_t header_bytes(int32_t n_tensors) { return 32 + 8 * (int64_t)n_tensors; }
+int64_t header_bytes(int32_t n_tensors) { return 40 + 8 * (int64_t)n_tensors; }
 
 template <class T>
 void put(uint8_t *base, int64_t &off, T v) {
@@ -354,7 +386,7 @@ extern "C" {
 int64_t adam_state_serialized_bytes(const adam_state *s) {
     if (!s) return fail(ADAM_EINVAL, "state is NULL");
     int64_t n = header_bytes(s->n_tensors);
-    for (int32_t b : buffers_of(s->layout.storage)) n += 16 + align8(buffer_of(s, b).bytes);
+    for (int32_t b : buffers_of(s->layout)) n += 16 + align8(buffer_of(s, b).bytes);
     return n + 16;
 }
 
@@ -373,9 +405,11 @@ int adam_state_save(adam_state *s, void *dst, int64_t nbytes, void *hip_stream) 
     put<int32_t>(out, off, s->layout.storage);
     put<int32_t>(out, off, s->layout.grad_dtype);
     put<int32_t>(out, off, s->layout.block_size);
+    put<uint32_t>(out, off, s->layout.options);
     put<int32_t>(out, off, s->n_tensors);
+    put<uint32_t>(out, off, 0u);
     for (int32_t k = 0; k < s->n_tensors; ++k) put<int64_t>(out, off, s->numels[k]);
-    const std::vector<int32_t> bufs = buffers_of(s->layout.storage);
+    const std::vector<int32_t> bufs = buffers_of(s->layout);
     hipError_t e;
     for (int32_t b : bufs) {
         const BufferView v = buffer_of(s, b);
@@ -401,19 +435,21 @@ int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip
     *out = nullptr;
     const uint8_t *in = static_cast<const uint8_t *>(src);
     int64_t off = 0;
-    if (nbytes < 32 + 16 || std::memcmp(in, kMagic, 8) != 0) return fail(ADAM_EINVAL, "not a serialized Adam state");
+    if (nbytes < 40 + 16 || std::memcmp(in, kMagic, 8) != 0) return fail(ADAM_EINVAL, "not a serialized Adam state");
     off = 8;
-    uint32_t version = 0, hbytes = 0;
+    uint32_t version = 0, hbytes = 0, hzero = 1;
     adam_layout lay{};
     int32_t n_tensors = 0;
     get(in, nbytes, off, version);
+    if (version != kFormatVersion) return fail(ADAM_EINVAL, "unsupported state format version " + std::to_string(version));
     get(in, nbytes, off, hbytes);
     get(in, nbytes, off, lay.storage);
     get(in, nbytes, off, lay.grad_dtype);
     get(in, nbytes, off, lay.block_size);
+    get(in, nbytes, off, lay.options);
     get(in, nbytes, off, n_tensors);
-    if (version != kFormatVersion) return fail(ADAM_EINVAL, "unsupported state format version " + std::to_string(version));
-    if (n_tensors < 0 || (int64_t)hbytes != header_bytes(n_tensors) || (int64_t)hbytes > nbytes - 16)
+    get(in, nbytes, off, hzero);
+    if (n_tensors < 0 || hzero != 0 || (int64_t)hbytes != header_bytes(n_tensors) || (int64_t)hbytes > nbytes - 16)
         return fail(ADAM_EINVAL, "corrupt state header");
     int rc = check_layout(&lay);
     if (rc) return rc;
@@ -425,8 +461,8 @@ int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip
     uint64_t want_hash = 0;
     std::memcpy(&want_hash, in + nbytes - 8, 8);
     if (stream_hash(in, nbytes - 8) != want_hash) return fail(ADAM_EINVAL, "serialized state checksum mismatch");
-    // records: exactly the storage mode's buffers, in order, with the sizes this layout implies
-    const std::vector<int32_t> bufs = buffers_of(lay.storage);
+    // records: exactly the layout's buffers, in order, with the sizes it implies
+    const std::vector<int32_t> bufs = buffers_of(lay);
     int64_t padded = 0, nblocks = 0;
     for (int64_t n : numels) {
         padded += pad16(n);
@@ -440,9 +476,9 @@ int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip
             return fail(ADAM_EINVAL, "truncated serialized state");
         int64_t expect = 0;
         switch (b) {
-        case ADAM_BUF_M_CODES: case ADAM_BUF_V_CODES: expect = padded; break;
-        case ADAM_BUF_M_SCALE: case ADAM_BUF_V_SCALE: expect = 4 * nblocks; break;
-        case ADAM_BUF_M_BF16: case ADAM_BUF_V_BF16: expect = 2 * padded; break;
+        case ADAM_BUF_M_CODES: case ADAM_BUF_V_CODES: case ADAM_BUF_VMAX_CODES: expect = padded; break;
+        case ADAM_BUF_M_SCALE: case ADAM_BUF_V_SCALE: case ADAM_BUF_VMAX_SCALE: expect = 4 * nblocks; break;
+        case ADAM_BUF_M_BF16: case ADAM_BUF_V_BF16: case ADAM_BUF_VMAX_BF16: expect = 2 * padded; break;
         default: expect = 4 * padded; break;
         }
         if ((int32_t)id != b || zero != 0 || (int64_t)len != expect)
@@ -520,7 +556,7 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
     if (!s) return fail(ADAM_EINVAL, "state is NULL");
     if (!expect) return fail(ADAM_EINVAL, "expected layout is NULL");
     if (expect->storage != s->layout.storage || expect->grad_dtype != s->layout.grad_dtype ||
-        expect->block_size != s->layout.block_size)
+        expect->block_size != s->layout.block_size || expect->options != s->layout.options)
         return fail(ADAM_EMODE, "layout differs from the one the state was created with");
     int rc = check_hparams(hp, s->layout.storage);
     if (rc) return rc;
@@ -587,6 +623,8 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
     a.v_state = s->v;
     a.m_scale = s->m_scale;
     a.v_scale = s->v_scale;
+    a.w_state = s->w;
+    a.w_scale = s->w_scale;
     a.step = (float)((double)hp->lr / bc1);
     a.ibc2 = (float)(1.0 / std::sqrt(bc2));
     a.decay = decoupled ? (float)(1.0 - (double)hp->lr * (double)hp->weight_decay) : 1.0f;
@@ -606,7 +644,8 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
     a.n_full = (uint32_t)s->n_full;
     a.n_all = (uint32_t)s->nblocks;
     Variant v{s->layout.storage, s->layout.grad_dtype == ADAM_GRAD_BF16, (hp->flags & ADAM_F_STOCHASTIC) != 0,
-              (hp->flags & ADAM_F_PERCENTILE) != 0, (hp->flags & ADAM_F_STATIC_SCALES) != 0};
+              (hp->flags & ADAM_F_PERCENTILE) != 0, (hp->flags & ADAM_F_STATIC_SCALES) != 0,
+              amsgrad(s->layout)};
     if ((e = launch_step(v, a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
     return ADAM_OK;
 }

@@ -38,6 +38,8 @@ def read_state(st):
     """All state buffers as numpy arrays named like the oracle's."""
     names = {"bf16": ["m_bf16", "v_bf16"], "q8": ["m_codes", "v_codes", "m_scale", "v_scale"],
              "q8_v_only": ["m_f32", "v_codes", "v_scale"]}[st.storage]
+    if st.amsgrad:
+        names += ["vmax_bf16"] if st.storage == "bf16" else ["vmax_codes", "vmax_scale"]
     out = {}
     for nm in names:
         t = ma.adam_state_read(st, nm)
@@ -95,13 +97,13 @@ def compare_buffer(name, got, want, stochastic, stats, where=""):
 
 
 def run_full_parity(numels, storage, grad_dtype, steps, hp, cfg_id=1, stats=None,
-                    grad_dist="normal", check_every_step=True, params=None):
+                    grad_dist="normal", check_every_step=True, params=None, amsgrad=False):
     """Full element-by-element comparison over `steps` steps from zero state."""
     stats = stats or Stats()
     params = params if params is not None else workloads.host_params(cfg_id, numels)
     dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
-    st = ma.adam_state_create(numels, storage, grad_dtype)
-    ost = oracle.OracleState(numels, storage, grad_bf16=(grad_dtype == "bf16"))
+    st = ma.adam_state_create(numels, storage, grad_dtype, amsgrad=amsgrad)
+    ost = oracle.OracleState(numels, storage, grad_bf16=(grad_dtype == "bf16"), amsgrad=amsgrad)
     for t in range(1, steps + 1):
         grads = workloads.host_grads(cfg_id, numels, t, dist=grad_dist, dtype=grad_dtype)
         ma.adam_step(st, dev_p, to_device_grads(grads, grad_dtype), t=t, **hp)
@@ -172,9 +174,9 @@ def run_sampled_parity(cfg, steps=None, n_random=800, log=print):
     host_p = _split(_gather(params, sel), sel)
     gdt = torch.bfloat16 if cfg.grad_dtype == "bf16" else torch.float32
     grads = [torch.empty(n, dtype=gdt, device="cuda") for n in numels]
-    st = ma.adam_state_create(numels, cfg.storage, cfg.grad_dtype)
+    st = ma.adam_state_create(numels, cfg.storage, cfg.grad_dtype, amsgrad=cfg.amsgrad)
     ob = oracle.OracleBlocks([(n, gidx) for _, _, n, gidx in sel], cfg.storage,
-                             grad_bf16=(cfg.grad_dtype == "bf16"))
+                             grad_bf16=(cfg.grad_dtype == "bf16"), amsgrad=cfg.amsgrad)
     for t in range(1, steps + 1):
         workloads.device_grads(cfg.cfg_id, numels, t, dist=cfg.grad_dist,
                                dtype=cfg.grad_dtype, out=grads)

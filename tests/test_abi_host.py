@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_structs_match_the_header_sizes():
-    assert ctypes.sizeof(B.adam_layout) == 12
+    assert ctypes.sizeof(B.adam_layout) == 16 and B.adam_layout.options.offset == 12
     assert ctypes.sizeof(B.adam_hparams) == 48
     assert B.adam_hparams.t.offset == 24 and B.adam_hparams.seed.offset == 40
 
@@ -44,12 +44,16 @@ def _pad16(n):
     return (n + 15) // 16 * 16
 
 
-@pytest.mark.parametrize("storage,e,s", [("bf16", 4, 0), ("q8", 2, 8), ("q8_v_only", 5, 4)])
-def test_state_bytes_closed_form(storage, e, s):
+@pytest.mark.parametrize("storage,e,s,ae,as_", [("bf16", 4, 0, 2, 0), ("q8", 2, 8, 1, 4),
+                                                ("q8_v_only", 5, 4, 1, 4)])
+def test_state_bytes_closed_form(storage, e, s, ae, as_):
     numels = [1, 17, 2048, 2049, 6001, 0, 1048576]
     want = sum(_pad16(n) * e + -(-n // 2048) * s for n in numels)
     assert ma.adam_state_bytes(numels, storage, "f32") == want
     assert ma.adam_state_bytes([], storage, "bf16") == 0
+    # AMSGrad: the running maximum of v stored as v is
+    extra = sum(_pad16(n) * ae + -(-n // 2048) * as_ for n in numels)
+    assert ma.adam_state_bytes(numels, storage, "f32", amsgrad=True) == want + extra
 
 
 def test_state_bytes_matches_the_pages_memory_claims():
@@ -81,6 +85,9 @@ def test_state_bytes_rejects_bad_arguments():
     lib = ma.library()
     assert lib.adam_state_bytes(-1, None, None) == -1
     assert lib.adam_state_bytes(1, None, ctypes.byref(B._layout("q8", "f32"))) == -1
+    n, arr = B._numels([5])
+    assert lib.adam_state_bytes(n, arr, ctypes.byref(B._layout("q8", "f32", 2048, 2))) == -1
+    assert "option" in ma.adam_last_error()
 
 
 def test_create_rejects_bad_arguments_before_any_device_call():
@@ -128,17 +135,20 @@ def _stream_hash(b):
     return h ^ (h >> 32)
 
 
-def _serialized(numels, storage=2, records=None, version=1):
+def _serialized(numels, storage=2, records=None, version=2, options=0, pad_word=0):
     import struct
     pad16 = [(n + 15) // 16 * 16 for n in numels]
     blocks = sum(-(-n // 2048) for n in numels)
     out = bytearray(b"MEAMSTAT")
-    out += struct.pack("<IIiiii", version, 32 + 8 * len(numels), storage, 0, 2048, len(numels))
+    out += struct.pack("<IIiiiIiI", version, 40 + 8 * len(numels), storage, 0, 2048, options,
+                       len(numels), pad_word)
     out += struct.pack(f"<{len(numels)}q", *numels)
     if records is None:
         P = sum(pad16)
         records = {2: [(0, P), (1, P), (2, 4 * blocks), (3, 4 * blocks)],
                    1: [(4, 2 * P), (5, 2 * P)], 3: [(1, P), (3, 4 * blocks), (6, 4 * P)]}[storage]
+        if options & 1:
+            records += [(9, 2 * P)] if storage == 1 else [(7, P), (8, 4 * blocks)]
     for bid, nb in records:
         out += struct.pack("<IIQ", bid, 0, nb) + bytes((nb + 7) // 8 * 8)
     out += struct.pack("<II", 0xFFFFFFFF, len(records))
@@ -155,7 +165,8 @@ def _load_rc(buf):
 
 
 @pytest.mark.parametrize("mutate", ["magic", "version", "truncate", "checksum", "payload",
-                                    "record_order", "record_size", "storage", "numel"])
+                                    "record_order", "record_size", "storage", "numel",
+                                    "options", "header_word", "amsgrad_records"])
 def test_load_rejects_malformed_streams_before_any_device_call(mutate):
     import struct
     numels = [5000, 17]
@@ -163,7 +174,15 @@ def test_load_rejects_malformed_streams_before_any_device_call(mutate):
     if mutate == "magic":
         bad = b"XEAMSTAT" + bytes(good[8:])
     elif mutate == "version":
-        bad = _serialized(numels, version=2)
+        bad = _serialized(numels, version=1)
+    elif mutate == "options":
+        bad = _serialized(numels, options=2)
+    elif mutate == "header_word":
+        bad = _serialized(numels, pad_word=1)
+    elif mutate == "amsgrad_records":
+        # claims the AMSGrad option but holds only the plain buffers
+        P = 5008 + 32
+        bad = _serialized(numels, options=1, records=[(0, P), (1, P), (2, 16), (3, 16)])
     elif mutate == "truncate":
         bad = bytes(good[:-24])
     elif mutate == "checksum":
@@ -184,16 +203,17 @@ def test_load_rejects_malformed_streams_before_any_device_call(mutate):
         bad = bytes(bad[:-8]) + struct.pack("<Q", _stream_hash(bytes(bad[:-8])))
     else:  # numel
         bad = bytearray(good)
-        bad[32:40] = struct.pack("<q", -3)
+        bad[40:48] = struct.pack("<q", -3)
         bad = bytes(bad[:-8]) + struct.pack("<Q", _stream_hash(bytes(bad[:-8])))
     rc, h = _load_rc(bytes(bad))
     assert rc == -1 and h is None, (mutate, ma.adam_last_error())
 
 
-def test_load_of_a_valid_stream_gets_past_validation():
+@pytest.mark.parametrize("storage,options", [(2, 0), (1, 0), (3, 0), (2, 1), (1, 1), (3, 1)])
+def test_load_of_a_valid_stream_gets_past_validation(storage, options):
     # a well-formed stream passes every host check; on a machine without a GPU
     # the first device call (state creation) is what fails
-    rc, h = _load_rc(_serialized([5000, 17]))
+    rc, h = _load_rc(_serialized([5000, 17], storage=storage, options=options))
     if rc == 0:
         ma.library().adam_state_destroy(h)
     else:

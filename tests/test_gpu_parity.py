@@ -11,6 +11,9 @@ gets and compares element by element (criteria in tests/parity.py):
     every tail block;
   * static scales (kept once set) on the ragged set, mixed with dynamic
     steps, and on the full-size Llama-7B set;
+  * AMSGrad (running maximum of v) in every storage mode on the ragged set,
+    on the full-size GPT-1.3B set with stochastic rounding, and through a
+    checkpoint;
   * edge cases: empty lists and zero-size tensors, a 2^32-1 element tensor,
     injected non-zero states, degenerate hyperparameters, pointer changes,
     a side stream, and the error paths.
@@ -128,6 +131,40 @@ def test_static_scales_set_late_and_mixed_with_dynamic_steps(storage):
     st.destroy()
 
 
+AMSGRAD_MODES = [
+    # storage, grad dtype, stochastic, percentile, static scales, decoupled, beta2
+    ("bf16", "f32", False, None, False, True, 0.9),
+    ("bf16", "bf16", False, None, False, False, 0.999),
+    ("q8", "f32", False, None, False, True, 0.9),
+    ("q8", "bf16", True, None, False, True, 0.9),
+    ("q8", "f32", False, 99.9, False, False, 0.9),
+    ("q8", "bf16", True, 99.9, True, True, 0.9),
+    ("q8_v_only", "f32", True, None, False, True, 0.999),
+    ("q8_v_only", "bf16", False, 99.9, False, True, 0.9),
+    ("q8_v_only", "f32", False, None, True, True, 0.9),
+]
+
+
+@pytest.mark.parametrize("storage,gdt,sr,pct,static,dec,b2", AMSGRAD_MODES)
+def test_ragged_set_amsgrad(storage, gdt, sr, pct, static, dec, b2):
+    # beta2 = 0.9 lets v fall below its running maximum within a few steps
+    log(f"ragged AMSGrad {storage} grads={gdt} sr={sr} pct={pct} static={static} "
+        f"decoupled={dec} beta2={b2}")
+    hp = dict(HP, beta2=b2, stochastic=sr, percentile=pct, static_scales=static, decoupled=dec,
+              seed=4321)
+    for dist in ("normal", "student_t3"):
+        stats = run_full_parity(RAGGED, storage, gdt, 10, hp, cfg_id=14, grad_dist=dist,
+                                amsgrad=True)
+        log(f"  {dist}: {stats}")
+
+
+def test_full_size_sampled_blocks_amsgrad():
+    cfg = dataclasses.replace(workloads.CONFIGS["gpt1p3b_q8_sr"], steps=3, amsgrad=True)
+    log(f"full-size {cfg.name} AMSGrad: {sum(cfg.numels())} params, {cfg.steps} steps")
+    stats = run_sampled_parity(cfg, log=log)
+    assert stats.codes >= stats.params >= cfg.steps * 800 * 1024
+
+
 def test_single_tensor_1m_q8_ten_steps():
     cfg = workloads.CONFIGS["single_q8"]
     log("single 1M q8 nearest-even, 10 steps")
@@ -211,15 +248,16 @@ def test_largest_tensor_last_blocks():
 
 
 @pytest.mark.parametrize("storage", ["bf16", "q8", "q8_v_only"])
-def test_step_from_injected_state(storage):
+@pytest.mark.parametrize("ams", [False, True])
+def test_step_from_injected_state(storage, ams):
     # arbitrary (non-trajectory) state: extreme codes, tiny / huge / zero scales
     numels = [2048, 5000, 17]
     rng = np.random.default_rng(21)
-    ost = oracle.OracleState(numels, storage)
+    ost = oracle.OracleState(numels, storage, amsgrad=ams)
     for name, buf in ost.buffers().items():
         if name == "m_codes":
             buf[:] = rng.integers(-127, 128, buf.size)
-        elif name == "v_codes":
+        elif name in ("v_codes", "vmax_codes"):
             buf[:] = rng.integers(0, 256, buf.size)
         elif name.endswith("scale"):
             buf[:] = (10.0 ** rng.uniform(-30, 2, buf.size)).astype(np.float32)
@@ -227,7 +265,7 @@ def test_step_from_injected_state(storage):
             buf[-1] = np.float32(2.0 ** -112)
         elif name.endswith("bf16"):
             x = (rng.standard_normal(buf.size) * 1e-3).astype(np.float32)
-            buf[:] = oracle.bf16_from_f32(np.abs(x) if name == "v_bf16" else x)
+            buf[:] = oracle.bf16_from_f32(x if name == "m_bf16" else np.abs(x))
         elif name == "m_f32":
             buf[:] = (rng.standard_normal(buf.size) * 1e-3).astype(np.float32)
     # padding entries stay zero, as the layout keeps them
@@ -237,7 +275,7 @@ def test_step_from_injected_state(storage):
             if not name.endswith("scale"):
                 buf[seg + n:seg + oracle.pad16(n)] = 0
         seg += oracle.pad16(n)
-    st = ma.adam_state_create(numels, storage)
+    st = ma.adam_state_create(numels, storage, amsgrad=ams)
     for name, buf in ost.buffers().items():
         src = torch.from_numpy(buf.view(np.int16) if name.endswith("bf16") else buf).cuda()
         ma.adam_state_write(st, name, src)
@@ -367,6 +405,11 @@ def test_error_paths_enqueue_nothing():
     with pytest.raises(ma.AdamError) as e:  # layout drift
         ma.adam_step(st, [p[:100]], [g[:100]], t=1, expect=("bf16", "f32"), **HP)
     assert e.value.code == -2
+    with pytest.raises(ma.AdamError) as e:  # AMSGrad option drift
+        ma.adam_step(st, [p[:100]], [g[:100]], t=1, expect=("q8", "f32", 2048, 1), **HP)
+    assert e.value.code == -2
+    with pytest.raises(ma.AdamError):  # absent buffer
+        ma.adam_state_read(st, "vmax_codes")
     with pytest.raises(ma.AdamError) as e:  # 4-byte offset pointer
         ma.adam_step(st, [p[1:101]], [g[:100]], t=1, **HP)
     assert e.value.code == -3
@@ -423,10 +466,12 @@ def test_alternating_gradient_buffers_beyond_the_table_cache():
     st.destroy()
 
 
-@pytest.mark.parametrize("storage,gdt,sr,pct", [("bf16", "f32", False, None),
-                                                ("q8", "bf16", True, None),
-                                                ("q8_v_only", "bf16", False, 99.9)])
-def test_checkpoint_resume_is_bit_exact(storage, gdt, sr, pct):
+@pytest.mark.parametrize("storage,gdt,sr,pct,ams", [("bf16", "f32", False, None, False),
+                                                    ("q8", "bf16", True, None, False),
+                                                    ("q8_v_only", "bf16", False, 99.9, False),
+                                                    ("bf16", "bf16", False, None, True),
+                                                    ("q8", "f32", True, 99.9, True)])
+def test_checkpoint_resume_is_bit_exact(storage, gdt, sr, pct, ams):
     # 4 steps, save; continue 3 steps (A); load the checkpoint into a new
     # state and run the same 3 steps from the saved params (B).  A == B bit
     # for bit, and both equal the oracle after 7 uninterrupted steps.
@@ -434,8 +479,8 @@ def test_checkpoint_resume_is_bit_exact(storage, gdt, sr, pct):
     hp = dict(HP, stochastic=sr, percentile=pct, seed=77)
     params = workloads.host_params(28, numels)
     dev_p = [torch.from_numpy(x.copy()).cuda() for x in params]
-    st = ma.adam_state_create(numels, storage, gdt)
-    ost = oracle.OracleState(numels, storage, grad_bf16=(gdt == "bf16"))
+    st = ma.adam_state_create(numels, storage, gdt, amsgrad=ams)
+    ost = oracle.OracleState(numels, storage, grad_bf16=(gdt == "bf16"), amsgrad=ams)
     grads = [workloads.host_grads(28, numels, t, dtype=gdt) for t in range(1, 8)]
     for t in range(1, 5):
         ma.adam_step(st, dev_p, to_device_grads(grads[t - 1], gdt), t=t, **hp)
@@ -444,9 +489,12 @@ def test_checkpoint_resume_is_bit_exact(storage, gdt, sr, pct):
     saved_p = [x.clone() for x in dev_p]
     # the stream's records are the state buffers, verbatim
     got = read_state(st)
-    off = 32 + 8 * len(numels)
-    for name in {"bf16": ["m_bf16", "v_bf16"], "q8": ["m_codes", "v_codes", "m_scale", "v_scale"],
-                 "q8_v_only": ["v_codes", "v_scale", "m_f32"]}[storage]:
+    off = 40 + 8 * len(numels)
+    names = {"bf16": ["m_bf16", "v_bf16"], "q8": ["m_codes", "v_codes", "m_scale", "v_scale"],
+             "q8_v_only": ["v_codes", "v_scale", "m_f32"]}[storage]
+    if ams:
+        names += ["vmax_bf16"] if storage == "bf16" else ["vmax_codes", "vmax_scale"]
+    for name in names:
         nb = int(np.frombuffer(blob[off + 8:off + 16].tobytes(), np.uint64)[0])
         assert nb == got[name].nbytes
         assert np.array_equal(blob[off + 16:off + 16 + nb], got[name].view(np.uint8)), name
@@ -454,7 +502,7 @@ def test_checkpoint_resume_is_bit_exact(storage, gdt, sr, pct):
     for t in range(5, 8):
         ma.adam_step(st, dev_p, to_device_grads(grads[t - 1], gdt), t=t, **hp)
     st2 = ma.adam_state_load(blob)
-    assert st2.numels == list(numels) and st2.storage == storage
+    assert st2.numels == list(numels) and st2.storage == storage and st2.amsgrad == ams
     for t in range(5, 8):
         ma.adam_step(st2, saved_p, to_device_grads(grads[t - 1], gdt), t=t, **hp)
     for t in range(1, 8):

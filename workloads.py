@@ -114,6 +114,7 @@ class Config:
     grad_dist: str          # "normal" | "student_t3" | "normal_outliers"
     steps: int
     hp: dict = field(default_factory=dict)
+    amsgrad: bool = False   # the state keeps the running maximum of v
 
     def shapes(self):
         return self.shapes_fn()
