@@ -367,6 +367,39 @@ struct SelectLds<true> {
     __device__ uint32_t *scratch() { return s; }
 };
 
+// ---------------------------------------------------------------- exact sqrt / divide
+// Correctly rounded square root and quotient for operands in a normal range,
+// without the range handling of the general sequences (which scale tiny or
+// huge operands and patch zeros, infinities and NaNs).  Where they apply
+// they perform the same operations as the general correctly rounded
+// sequences, so the results are the same bits.
+//
+// sqrt_rn: x in [2^-96, 2^128).  The hardware square root is within one ulp
+// of sqrt(x), so the rounded root is it or a neighbour; the sign of the
+// exact residual x - s' * s (one fma) tells which: x <= s_- * s means sqrt(x)
+// lies below the midpoint of s_- and s, x > s_+ * s that it lies above the
+// midpoint of s and s_+ (x, s_- * s and s * s_+ sit on a grid too coarse for
+// x to fall strictly between a product and its midpoint square).
+__device__ __forceinline__ float sqrt_rn(float x) {
+    const float s = __builtin_amdgcn_sqrtf(x);
+    const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+    const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+    float r = fmaf(-sm, s, x) <= 0.0f ? sm : s;
+    return fmaf(-sp, s, x) > 0.0f ? sp : r;
+}
+
+// div_rn: d in [2^-40, 2^77], |n| in [2^-40, 2^40] (quotient and reciprocal
+// normal, no intermediate over- or underflow): the hardware reciprocal, one
+// Newton step, and two quotient corrections whose remainders n - d*q are
+// exact (fma).
+__device__ __forceinline__ float div_rn(float n, float d) {
+    float r = __builtin_amdgcn_rcpf(d);
+    r = fmaf(fmaf(-d, r, 1.0f), r, r);
+    float q = n * r;
+    q = fmaf(fmaf(-d, q, n), r, q);
+    return fmaf(fmaf(-d, q, n), r, q);
+}
+
 // Codes of four unsigned values x[b..b+3] (v, or the AMSGrad maximum) packed
 // into the bytes of one word; u: the group's four Philox words, of which the
 // 16 bits at `shift` are the draws.
@@ -403,7 +436,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                                               BlockLds &lds, SelectLds<kPct> &sel) {
     constexpr bool kQuantM = (kStore == kStoreQ8);
     const int tid = threadIdx.x;
-    float p[kItems], g[kItems], mo[kItems], vo[kItems], wo[kAms ? kItems : 1];
+    float p[kItems], g[kItems], mo[kItems], vo[kItems], wo[kItems];  // wo: AMSGrad only
 
     // ---- decode
     constexpr float Rm = 1.0f / 127.0f;
@@ -436,22 +469,50 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
     }
     float mmax = 0.0f, vmax = 0.0f, wmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const float gi = g[i];
-        const float m = fmaf(a.beta1, mo[i], a.omb1 * gi);
-        const float v = fmaf(a.beta2, vo[i], a.omb2 * (gi * gi));
-        float vd = v;  // the second moment the denominator uses
-        if constexpr (kAms) {
-            vd = fmaxf(wo[i], v);
-            wo[i] = vd;
-            wmax = fmaxf(wmax, vd);
+    for (int j = 0; j < kGroups; ++j) {
+        // moments of the 4-element group
+        float small = __builtin_inff(), big = 0.0f;  // min of |m| and v, max of |m|
+#pragma unroll
+        for (int i = 4 * j; i < 4 * j + 4; ++i) {
+            const float gi = g[i];
+            const float m = fmaf(a.beta1, mo[i], a.omb1 * gi);
+            const float v = fmaf(a.beta2, vo[i], a.omb2 * (gi * gi));
+            if constexpr (kAms) {
+                wo[i] = fmaxf(wo[i], v);  // the second moment the denominator uses
+                wmax = fmaxf(wmax, wo[i]);
+            }
+            mo[i] = m;
+            vo[i] = v;
+            vmax = fmaxf(vmax, v);
+            big = fmaxf(big, fabsf(m));
+            if constexpr (kAms) small = fminf(small, fminf(fabsf(m), wo[i]));
+            else small = fminf(small, fminf(fabsf(m), v));
         }
-        const float den = fmaf(sqrtf(vd), a.ibc2, a.eps);
-        p[i] = fmaf(-a.step, m / den, p[i] * a.decay);
-        mo[i] = m;
-        vo[i] = v;
-        mmax = fmaxf(mmax, fabsf(m));
-        vmax = fmaxf(vmax, v);
+        mmax = fmaxf(mmax, big);
+        // p = p*decay - step * m / (sqrt(v) * ibc2 + eps).  When every lane's
+        // group lies in the normal range (|m| and v at least 2^-40, |m| at
+        // most 2^40, so that sqrt(v) * ibc2 + eps is in [2^-40, 2^77] given
+        // ibc2 <= 2^12 and eps in [2^-40, 2^20]) the wave takes the short
+        // sequences, otherwise the general ones.  Same bits either way; one
+        // decision per group lets a group's update start while the next
+        // group's loads are still in flight.  The percentile variants (whose
+        // radix selects dominate) measured faster without the decision and
+        // always take the general sequences.
+        const float(&vden)[kItems] = kAms ? wo : vo;
+        const bool in_range = a.fast_ok && small >= 0x1p-40f && big <= 0x1p40f;
+        if (!kPct && __all(in_range)) {
+#pragma unroll
+            for (int i = 4 * j; i < 4 * j + 4; ++i) {
+                const float den = fmaf(sqrt_rn(vden[i]), a.ibc2, a.eps);
+                p[i] = fmaf(-a.step, div_rn(mo[i], den), p[i] * a.decay);
+            }
+        } else {
+#pragma unroll
+            for (int i = 4 * j; i < 4 * j + 4; ++i) {
+                const float den = fmaf(sqrtf(vden[i]), a.ibc2, a.eps);
+                p[i] = fmaf(-a.step, mo[i] / den, p[i] * a.decay);
+            }
+        }
     }
 
     // ---- store params

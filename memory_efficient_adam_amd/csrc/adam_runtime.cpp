@@ -635,6 +635,7 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
     a.eps = hp->eps;
     a.wd = hp->weight_decay;
     a.l2 = decoupled ? 0u : 1u;
+    a.fast_ok = (hp->eps >= 0x1p-40f && hp->eps <= 0x1p20f) ? 1u : 0u;
     a.pfrac = (double)hp->percentile / 100.0;
     a.seed_lo = (uint32_t)hp->seed;
     a.seed_hi = (uint32_t)(hp->seed >> 32);

@@ -165,6 +165,41 @@ def test_full_size_sampled_blocks_amsgrad():
     assert stats.codes >= stats.params >= cfg.steps * 800 * 1024
 
 
+@pytest.mark.parametrize("storage", ["bf16", "q8", "q8_v_only"])
+@pytest.mark.parametrize("eps", [1e-8, 2.0 ** -40, 1e-13, 1.0, 2.0 ** 20, 1e7])
+def test_mixed_magnitudes_in_one_block(storage, eps):
+    # within each block some waves hold only ordinary values and others tiny
+    # (1e-20), zero or huge (1e15) gradients, and eps sits inside, on and
+    # beyond the range where the update's short exact sqrt/divide applies:
+    # every element must still match the oracle
+    numels = [2048 * 3, 5000, 300]
+    log(f"mixed magnitudes {storage} eps={eps}")
+    params = workloads.host_params(31, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, storage, "f32")
+    ost = oracle.OracleState(numels, storage)
+    hp = dict(HP, eps=eps)
+    stats = Stats()
+    for t in range(1, 6):
+        grads = workloads.host_grads(31, numels, t)
+        for g in grads:
+            g[64:128] = 1e-20                 # one wave's lanes of the first group
+            g[1024 + 256:1024 + 300] = 0.0     # part of another wave
+            g[700:710] *= 1e18                 # |m| beyond 2^40
+            g[1600:1602] = 1e-30
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t} tensor {k}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, False, stats, f"t={t}")
+    log(f"  {stats}")
+    assert stats.params_exact == stats.params
+    st.destroy()
+
+
 def test_single_tensor_1m_q8_ten_steps():
     cfg = workloads.CONFIGS["single_q8"]
     log("single 1M q8 nearest-even, 10 steps")
