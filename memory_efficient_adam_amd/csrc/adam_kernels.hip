@@ -207,24 +207,37 @@ __device__ uint32_t block_select(const uint32_t (&key)[kItems], uint32_t rank, u
 // Code magnitude for |x| = a with statistic A and r = fl(qmax/A) (A >= kTiny).
 // For a < A, a <= A(1 - 2^-24) and r <= (qmax/A)(1 + 2^-24), so y = fl(a*r) <=
 // qmax: neither rounding can pass qmax (at y = qmax the fraction is 0), and
-// only a >= A -- possible with the percentile statistic, or at the block
-// maximum under stochastic rounding, where y may fall just below qmax --
-// needs the end pin (kPin).
-//
+// only a >= A -- possible with the percentile statistic or a kept scale, or
+// at the block maximum, where y may fall just below qmax -- needs the end
+// pin.  kEnd selects how it is applied:
+//   kPinEnd:   k = qmax wherever a >= A (a compare and a select);
+//   kClampEnd: y clamped to qmax before rounding (one min) -- the same codes
+//              when qmax = 127: at a >= A, y >= fl(A*r) >= 127 - 2^-17 (A*r
+//              is within 127 * 2^-24 < 2^-17 of 127, the spacing below 127
+//              being 2^-17), and both roundings take any y in
+//              [127 - 2^-17, 127] to 127 (for stochastic rounding ceil(y *
+//              2^16) = 127 * 2^16 there).  Not for qmax = 255: the spacing
+//              below 255 is 2^-16, and y = 255 - 2^-16 rounds stochastically
+//              to 254 for the draw 65535.
+//   kNoEnd:    nothing (only a = A reaches y near qmax, and nearest-even
+//              rounding takes it to qmax).
 // Stochastic rounding: floor(y) + [u16 * 2^-16 < frac(y)] is computed as
 // (ceil(y * 2^16) + 65535 - u16) >> 16.  With Y = y * 2^16 (exact, Y < 2^24)
 // = 2^16 floor(y) + F, u16 < F holds iff u16 < ceil(F), iff the low 16 bits of
 // ceil(Y) + 65535 - u16 carry into bit 16.
-template <bool kSR, bool kPin>
+enum EndRule { kNoEnd, kPinEnd, kClampEnd };
+
+template <bool kSR, EndRule kEnd>
 __device__ __forceinline__ uint32_t code_magnitude(float a, float A, float r, uint32_t qmax, uint32_t u16) {
-    const float y = a * r;
+    float y = a * r;
+    if constexpr (kEnd == kClampEnd) y = fminf(y, (float)qmax);
     uint32_t k;
     if constexpr (kSR) {
         k = ((uint32_t)ceilf(y * 65536.0f) + (0xFFFFu - u16)) >> 16;
     } else {
         k = (uint32_t)rintf(y);
     }
-    if constexpr (kPin) k = a >= A ? qmax : k;
+    if constexpr (kEnd == kPinEnd) k = a >= A ? qmax : k;
     return k;
 }
 
@@ -411,7 +424,7 @@ __device__ __forceinline__ uint32_t pack_u8(const float (&x)[kItems], int b, flo
     for (int k = 0; k < 4; ++k) {
         const float ax = fabsf(x[b + k]);
         if constexpr (kSR) {
-            c |= code_magnitude<true, true>(ax, pin, r, 255u, (u[k] >> shift) & 0xFFFFu) << (8 * k);
+            c |= code_magnitude<true, kPinEnd>(ax, pin, r, 255u, (u[k] >> shift) & 0xFFFFu) << (8 * k);
         } else {
             // nearest-even rounding, clamped to [0, 255], packed into byte k: the
             // clamp is the end pin (|x| >= A gives y >= 254.99998)
@@ -608,7 +621,6 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         const float rw = (!kAms || wzero) ? 0.0f : 255.0f / Awn;
         // a zero block has r = 0, so y = 0 and every code is 0; its pin
         // threshold is +inf so that the end pin never fires
-        const float pin_m = mzero ? __builtin_inff() : Amn;
         const float pin_v = vzero ? __builtin_inff() : Avn;
         const float pin_w = wzero ? __builtin_inff() : Awn;
 
@@ -639,7 +651,8 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const float x = mo[4 * j + k];
-                    const uint32_t q = code_magnitude<kSR, kPin>(fabsf(x), pin_m, rm, 127u, rnd[k] & 0xFFFFu);
+                    const uint32_t q = code_magnitude<kSR, kPin ? kClampEnd : kNoEnd>(fabsf(x), Amn, rm, 127u,
+                                                                                      rnd[k] & 0xFFFFu);
                     const uint32_t qs = x < 0.0f ? 0u - q : q;  // -0 gives 0
                     cm |= (qs & 0xFFu) << (8 * k);
                 }
