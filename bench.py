@@ -74,9 +74,10 @@ def traffic_for(workload):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(cfg, hp, steps=1):
-    """The oracle, as it is, on one full step of the same workload (single
-    thread), same recipe of inputs generated on the host."""
+def cpu_baseline(cfg, hp, min_seconds=10.0, max_steps=20):
+    """The oracle, as it is, on whole steps of the same workload (single
+    thread), same recipe of inputs generated on the host: steps are run
+    until at least min_seconds of oracle time (input generation untimed)."""
     import numpy as np  # noqa: F401
     import oracle
     import workloads
@@ -85,11 +86,13 @@ def cpu_baseline(cfg, hp, steps=1):
     st = oracle.OracleState(numels, cfg.storage, grad_bf16=(cfg.grad_dtype == "bf16"),
                             amsgrad=cfg.amsgrad)
     elapsed = 0.0
-    for t in range(1, steps + 1):
-        grads = workloads.host_grads(cfg.cfg_id, numels, t, dist=cfg.grad_dist,
+    steps = 0
+    while elapsed < min_seconds and steps < max_steps:
+        steps += 1
+        grads = workloads.host_grads(cfg.cfg_id, numels, steps, dist=cfg.grad_dist,
                                      dtype=cfg.grad_dtype)
         t0 = time.perf_counter()
-        st.step(params, grads, t=t, **hp)
+        st.step(params, grads, t=steps, **hp)
         elapsed += time.perf_counter() - t0
     n = sum(numels)
     return {"value": round(n * steps / elapsed / 1e9, 5), "unit": "Gparams/s", "cores": 1,
@@ -161,14 +164,20 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
+    # one event before each step and one after the last, all on the launch
+    # stream: per-step times as well as the whole timed region
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for k in range(args.steps):
         t += 1
         ma.adam_step(st, params, gsets[t % len(gsets)], t=t, stream=stream, **hp)
+        marks[k + 1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = start.elapsed_time(end) / args.steps
+    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
     sec = ms / 1e3
 
     alg = algorithmic_bytes(cfg)
@@ -185,6 +194,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 5),
+        "ms_per_step_min": round(per_step[0], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
