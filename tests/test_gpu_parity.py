@@ -200,6 +200,54 @@ def test_mixed_magnitudes_in_one_block(storage, eps):
     st.destroy()
 
 
+def _random_case(i):
+    rng = np.random.default_rng([4242, i])
+    storage = ["bf16", "q8", "q8_v_only"][i % 3]
+    q8 = storage != "bf16"
+    case = dict(
+        storage=storage,
+        grad_dtype=["f32", "bf16"][int(rng.integers(2))],
+        amsgrad=bool(rng.integers(2)),
+        numels=[int(x) for x in rng.choice([0, 1, 15, 16, 17, 2047, 2048, 2049, 4100, 6144, 9001],
+                                           size=int(rng.integers(1, 5)))],
+        t0=int(rng.choice([1, 2, 1000, 100000])),
+        dist=["normal", "student_t3"][int(rng.integers(2))],
+        hp=dict(lr=float(rng.choice([1e-4, 1e-3, 1e-1])), beta1=float(rng.choice([0.0, 0.5, 0.9, 0.99])),
+                beta2=float(rng.choice([0.9, 0.99, 0.999, 0.9999])),
+                eps=float(rng.choice([1e-8, 1e-6, 1e-12, 1e-3])),
+                weight_decay=float(rng.choice([0.0, 0.01, 0.1])), decoupled=bool(rng.integers(2)),
+                stochastic=q8 and bool(rng.integers(2)),
+                percentile=(float(rng.choice([0.0, 50.0, 99.0, 99.9, 100.0]))
+                            if q8 and rng.integers(2) else None),
+                static_scales=q8 and bool(rng.integers(3) == 0), seed=int(rng.integers(2 ** 63))))
+    return case
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configurations(i):
+    c = _random_case(i)
+    numels, hp, gdt = c["numels"], c["hp"], c["grad_dtype"]
+    log(f"random case {i}: {c}")
+    params = workloads.host_params(500 + i, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, c["storage"], gdt, amsgrad=c["amsgrad"])
+    ost = oracle.OracleState(numels, c["storage"], grad_bf16=(gdt == "bf16"), amsgrad=c["amsgrad"])
+    stats = Stats()
+    for t in range(c["t0"], c["t0"] + 4):
+        grads = workloads.host_grads(500 + i, numels, t, dist=c["dist"], dtype=gdt)
+        ma.adam_step(st, dev_p, to_device_grads(grads, gdt), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t} tensor {k}")
+        if sum(numels):
+            got = read_state(st)
+            for nm, want in ost.buffers().items():
+                compare_buffer(nm, got[nm], want, hp["stochastic"], stats, f"t={t}")
+    log(f"  {stats}")
+    st.destroy()
+
+
 def test_single_tensor_1m_q8_ten_steps():
     cfg = workloads.CONFIGS["single_q8"]
     log("single 1M q8 nearest-even, 10 steps")
