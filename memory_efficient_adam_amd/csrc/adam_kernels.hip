@@ -4,8 +4,9 @@
 // reads the block's params, grads, stored moments and old scales once,
 // keeps the updated moments in registers, reduces the block statistic
 // (DPP cross-lane steps + one cross-wave LDS step; an LDS radix select for
-// the percentile statistic), requantizes and writes params, moments and the
-// new scales once.  The step is a streaming map over HBM (14-20 bytes per
+// the percentile statistic; skipped for a moment whose static scale is
+// already set), requantizes and writes params, moments and the new scales
+// once.  With AMSGrad the running maximum of v travels the same way as v.  The step is a streaming map over HBM (14-20 bytes per
 // parameter, ~1.5 flop/byte), so there is no MFMA work; what matters is
 // coalesced 16-byte loads, enough bytes in flight per CU and a VALU budget
 // of roughly 100 instructions per element at the bandwidth target.
@@ -15,7 +16,9 @@
 // (dequantize -> bias-corrected Adam -> quantize, block-wise, signed m /
 // unsigned v, dynamic scales, optional fp32 m, stochastic rounding,
 // percentile scaling); "perf(training): make BF16-Adam fused-compatible"
-// (AiDotNet PR #1745) -- bf16 moment buffers in one fused Adam/AdamW kernel.
+// (AiDotNet PR #1745) -- bf16 moment buffers in one fused Adam/AdamW kernel,
+// and AMSGrad named there as a variant still without one (built after
+// Reddi, Kale & Kumar, "On the Convergence of Adam and Beyond", ICLR 2018).
 // Philox4x32-10 follows Salmon et al., "Parallel Random Numbers: As Easy as
 // 1, 2, 3" (SC'11).
 //
@@ -440,7 +443,7 @@ __device__ __forceinline__ float uniform(float x) {
 
 // Decode, update, store params; block statistic; requantize and store state.
 // kStatic: a moment whose stored scale is already set (>= kTiny) keeps it and
-// skips its statistic; values at or beyond it saturate through the end pin.
+// skips its statistic; values at or beyond it saturate through the end rule.
 // kAms: AMSGrad -- the running maximum w of v is decoded, updated to
 // max(w, v), used in the denominator and stored as v is, with its own scale.
 template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kAms, bool kFull>
