@@ -52,11 +52,17 @@ def algorithmic_bytes(cfg):
 
 
 def kernel_source_hash():
-    """sha256 over the sources that define the step kernel."""
+    """sha256 over the code of the sources that define the step kernel
+    (comments and whitespace removed, so that editing a comment does not
+    retire the counter readings)."""
+    import re
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 
