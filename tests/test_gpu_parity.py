@@ -266,7 +266,7 @@ def test_full_size_sampled_blocks_static_scales():
 
 
 @pytest.mark.parametrize("name", ["vit_bf16", "vit_q8", "gpt1p3b_q8_sr",
-                                  "llama7b_mf32_vq8_pct"])
+                                  "llama7b_mf32_vq8_pct", "llama7b_shard8_mf32_vq8_pct"])
 def test_full_size_sampled_blocks(name):
     cfg = workloads.CONFIGS[name]
     log(f"full-size {name}: {sum(cfg.numels())} params, {cfg.steps} steps")

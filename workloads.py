@@ -89,6 +89,30 @@ def llama_7b_shapes():
     return s
 
 
+def zero1_shard_shapes(shapes, rank, n_ranks, block=2048):
+    """Rank `rank`'s share of a parameter set under ZeRO-1 block sharding:
+    the blocks of all tensors, in order, split into n_ranks contiguous runs of
+    (nearly) equal length; a tensor cut by a run boundary contributes the
+    1-D slice of its flattened elements that lies in the run (cuts fall on
+    block boundaries, so every block of the shard is a block of the set)."""
+    sizes = [int(np.prod(shp)) for _, shp in shapes]
+    total = sum((n + block - 1) // block for n in sizes)
+    lo, hi = total * rank // n_ranks, total * (rank + 1) // n_ranks
+    out, first = [], 0  # first: global index of the tensor's first block
+    for (name, _), n in zip(shapes, sizes):
+        nb = (n + block - 1) // block
+        b0, b1 = max(lo, first) - first, min(hi, first + nb) - first
+        if b0 < b1:
+            s0, s1 = b0 * block, min(n, b1 * block)
+            out.append((f"{name}[{s0}:{s1}]", (s1 - s0,)))
+        first += nb
+    return out
+
+
+def llama_7b_shard8_shapes():
+    return zero1_shard_shapes(llama_7b_shapes(), 0, 8)
+
+
 RAGGED_SIZES = (1, 3, 4, 5, 16, 17, 1000, 1023, 1024, 1025, 2047, 2048, 2049,
                 4096, 6001, 12289)
 
@@ -138,6 +162,10 @@ CONFIGS = {
     "llama7b_mf32_vq8_pct": Config(5, "llama7b_mf32_vq8_pct", llama_7b_shapes, "q8_v_only",
                                    "bf16", "normal_outliers", 3,
                                    dict(_ADAMW, percentile=99.9)),
+    # one GPU's share of the Llama-7B set under 8-way ZeRO-1 block sharding
+    "llama7b_shard8_mf32_vq8_pct": Config(6, "llama7b_shard8_mf32_vq8_pct", llama_7b_shard8_shapes,
+                                          "q8_v_only", "bf16", "normal_outliers", 3,
+                                          dict(_ADAMW, percentile=99.9)),
 }
 
 
