@@ -67,6 +67,21 @@ int fail(int code, const std::string &msg) {
     return code;
 }
 
+// Runs an entry point's body: a host allocation failure inside it comes back
+// as ADAM_ENOMEM instead of escaping through the C ABI.
+template <class F>
+auto guarded(F &&body) noexcept -> decltype(body()) {
+    try {
+        return body();
+    } catch (const std::bad_alloc &) {
+        try { g_error = "host allocation failed"; } catch (...) { g_error.clear(); }
+        return ADAM_ENOMEM;
+    } catch (...) {
+        try { g_error = "unexpected host exception"; } catch (...) { g_error.clear(); }
+        return ADAM_EDEVICE;
+    }
+}
+
 int64_t pad16(int64_t n) { return (n + 15) / 16 * 16; }
 
 int64_t blocks_of(int64_t n) { return (n + kBlock - 1) / kBlock; }
@@ -217,106 +232,118 @@ int64_t adam_state_bytes(int32_t n_tensors, const int64_t *numels, const adam_la
 
 int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels, const adam_layout *layout,
                       void *hip_stream) {
-    if (!out) return fail(ADAM_EINVAL, "out is NULL");
-    *out = nullptr;
-    int rc = check_numels(n_tensors, numels);
-    if (rc) return rc;
-    if ((rc = check_layout(layout))) return rc;
+    return guarded([&]() -> int {
+        if (!out) return fail(ADAM_EINVAL, "out is NULL");
+        *out = nullptr;
+        int rc = check_numels(n_tensors, numels);
+        if (rc) return rc;
+        if ((rc = check_layout(layout))) return rc;
 
-    adam_state *s = new (std::nothrow) adam_state();
-    if (!s) return fail(ADAM_ENOMEM, "host allocation failed");
-    hipError_t e = hipGetDevice(&s->device);
-    if (e != hipSuccess) {
-        s->device = -1;
-        release(s);
-        return hip_fail(e, "hipGetDevice");
-    }
-    s->layout = *layout;
-    s->n_tensors = n_tensors;
-    s->numels.assign(numels, numels + n_tensors);
-    // descriptors: full blocks first, then each tensor's ragged last block;
-    // scale slots keep the tensor-major block numbering
-    std::vector<BlockDesc> desc, tails;
-    int64_t slot = 0;
-    for (int32_t k = 0; k < n_tensors; ++k) {
-        const int64_t n = numels[k];
-        for (int64_t b = 0; b * kBlock < n; ++b, ++slot) {
-            const int64_t len = std::min<int64_t>(kBlock, n - b * kBlock);
-            const BlockDesc d{(uint32_t)((s->padded + b * kBlock) / 16), (uint32_t)k,
-                              (uint32_t)((b << kBlockBits) | (len - 1)), (uint32_t)slot};
-            (len == kBlock ? desc : tails).push_back(d);
+        int64_t total_blocks = 0, total_padded = 0;
+        for (int32_t k = 0; k < n_tensors; ++k) {
+            total_blocks += blocks_of(numels[k]);
+            total_padded += pad16(numels[k]);
         }
-        s->padded += pad16(n);
-    }
-    s->n_full = (int64_t)desc.size();
-    desc.insert(desc.end(), tails.begin(), tails.end());
-    s->nblocks = (int64_t)desc.size();
-    if (s->nblocks >= (int64_t(1) << 32) || s->padded / 16 >= (int64_t(1) << 32)) {
-        release(s);
-        return fail(ADAM_EINVAL, "state too large: more than 2^32 - 1 blocks or 2^36 elements");
-    }
+        if (total_blocks >= (int64_t(1) << 32) || total_padded / 16 >= (int64_t(1) << 32))
+            return fail(ADAM_EINVAL, "state too large: more than 2^32 - 1 blocks or 2^36 elements");
 
-    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-    const int32_t st = layout->storage;
-    const int64_t m_bytes = st == ADAM_STORE_BF16 ? 2 * s->padded : (st == ADAM_STORE_Q8 ? s->padded : 4 * s->padded);
-    const int64_t v_bytes = st == ADAM_STORE_BF16 ? 2 * s->padded : s->padded;
-    if ((rc = alloc_zeroed(&s->m, m_bytes, stream)) || (rc = alloc_zeroed(&s->v, v_bytes, stream))) {
-        release(s);
-        return rc;
-    }
-    if (st == ADAM_STORE_Q8 && (rc = alloc_zeroed((void **)&s->m_scale, 4 * s->nblocks, stream))) {
-        release(s);
-        return rc;
-    }
-    if (st != ADAM_STORE_BF16 && (rc = alloc_zeroed((void **)&s->v_scale, 4 * s->nblocks, stream))) {
-        release(s);
-        return rc;
-    }
-    if (amsgrad(*layout) &&
-        ((rc = alloc_zeroed(&s->w, st == ADAM_STORE_BF16 ? 2 * s->padded : s->padded, stream)) ||
-         (st != ADAM_STORE_BF16 && (rc = alloc_zeroed((void **)&s->w_scale, 4 * s->nblocks, stream))))) {
-        release(s);
-        return rc;
-    }
-    if (s->nblocks > 0) {
-        if (hipMalloc((void **)&s->d_desc, desc.size() * sizeof(BlockDesc)) != hipSuccess) {
-            (void)hipGetLastError();
-            release(s);
-            return fail(ADAM_ENOMEM, "hipMalloc of the descriptor table failed");
-        }
-        e = hipMemcpyAsync(s->d_desc, desc.data(), desc.size() * sizeof(BlockDesc), hipMemcpyHostToDevice, stream);
+        adam_state *s = new (std::nothrow) adam_state();
+        if (!s) return fail(ADAM_ENOMEM, "host allocation failed");
+        hipError_t e = hipGetDevice(&s->device);
         if (e != hipSuccess) {
+            s->device = -1;
             release(s);
-            return hip_fail(e, "descriptor upload");
+            return hip_fail(e, "hipGetDevice");
         }
-    }
-    if (n_tensors > 0) {
-        const size_t tbytes = (size_t)n_tensors * sizeof(TensorRef);
-        for (int i = 0; i < kTableSlots; ++i) {
-            if (hipMalloc((void **)&s->tables[i].dev, tbytes) != hipSuccess) {
+        s->layout = *layout;
+        s->n_tensors = n_tensors;
+        // descriptors: full blocks first, then each tensor's ragged last block;
+        // scale slots keep the tensor-major block numbering
+        std::vector<BlockDesc> desc, tails;
+        try {
+            s->numels.assign(numels, numels + n_tensors);
+            desc.reserve((size_t)total_blocks);
+            int64_t slot = 0;
+            for (int32_t k = 0; k < n_tensors; ++k) {
+                const int64_t n = numels[k];
+                for (int64_t b = 0; b * kBlock < n; ++b, ++slot) {
+                    const int64_t len = std::min<int64_t>(kBlock, n - b * kBlock);
+                    const BlockDesc d{(uint32_t)((s->padded + b * kBlock) / 16), (uint32_t)k,
+                                      (uint32_t)((b << kBlockBits) | (len - 1)), (uint32_t)slot};
+                    (len == kBlock ? desc : tails).push_back(d);
+                }
+                s->padded += pad16(n);
+            }
+            s->n_full = (int64_t)desc.size();
+            desc.insert(desc.end(), tails.begin(), tails.end());
+        } catch (const std::bad_alloc &) {
+            release(s);
+            return fail(ADAM_ENOMEM, "host allocation of the descriptor table failed");
+        }
+        s->nblocks = (int64_t)desc.size();
+
+        hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+        const int32_t st = layout->storage;
+        const int64_t m_bytes = st == ADAM_STORE_BF16 ? 2 * s->padded : (st == ADAM_STORE_Q8 ? s->padded : 4 * s->padded);
+        const int64_t v_bytes = st == ADAM_STORE_BF16 ? 2 * s->padded : s->padded;
+        if ((rc = alloc_zeroed(&s->m, m_bytes, stream)) || (rc = alloc_zeroed(&s->v, v_bytes, stream))) {
+            release(s);
+            return rc;
+        }
+        if (st == ADAM_STORE_Q8 && (rc = alloc_zeroed((void **)&s->m_scale, 4 * s->nblocks, stream))) {
+            release(s);
+            return rc;
+        }
+        if (st != ADAM_STORE_BF16 && (rc = alloc_zeroed((void **)&s->v_scale, 4 * s->nblocks, stream))) {
+            release(s);
+            return rc;
+        }
+        if (amsgrad(*layout) &&
+            ((rc = alloc_zeroed(&s->w, st == ADAM_STORE_BF16 ? 2 * s->padded : s->padded, stream)) ||
+             (st != ADAM_STORE_BF16 && (rc = alloc_zeroed((void **)&s->w_scale, 4 * s->nblocks, stream))))) {
+            release(s);
+            return rc;
+        }
+        if (s->nblocks > 0) {
+            if (hipMalloc((void **)&s->d_desc, desc.size() * sizeof(BlockDesc)) != hipSuccess) {
                 (void)hipGetLastError();
                 release(s);
-                return fail(ADAM_ENOMEM, "pointer table allocation failed");
+                return fail(ADAM_ENOMEM, "hipMalloc of the descriptor table failed");
+            }
+            e = hipMemcpyAsync(s->d_desc, desc.data(), desc.size() * sizeof(BlockDesc), hipMemcpyHostToDevice, stream);
+            if (e != hipSuccess) {
+                release(s);
+                return hip_fail(e, "descriptor upload");
             }
         }
-        for (int i = 0; i < kStageSlots; ++i) {
-            if (hipHostMalloc((void **)&s->stage[i], tbytes, hipHostMallocDefault) != hipSuccess) {
-                (void)hipGetLastError();
-                release(s);
-                return fail(ADAM_ENOMEM, "pinned staging allocation failed");
+        if (n_tensors > 0) {
+            const size_t tbytes = (size_t)n_tensors * sizeof(TensorRef);
+            for (int i = 0; i < kTableSlots; ++i) {
+                if (hipMalloc((void **)&s->tables[i].dev, tbytes) != hipSuccess) {
+                    (void)hipGetLastError();
+                    release(s);
+                    return fail(ADAM_ENOMEM, "pointer table allocation failed");
+                }
             }
-            if ((e = hipEventCreateWithFlags(&s->stage_done[i], hipEventDisableTiming)) != hipSuccess) {
-                release(s);
-                return hip_fail(e, "hipEventCreate");
+            for (int i = 0; i < kStageSlots; ++i) {
+                if (hipHostMalloc((void **)&s->stage[i], tbytes, hipHostMallocDefault) != hipSuccess) {
+                    (void)hipGetLastError();
+                    release(s);
+                    return fail(ADAM_ENOMEM, "pinned staging allocation failed");
+                }
+                if ((e = hipEventCreateWithFlags(&s->stage_done[i], hipEventDisableTiming)) != hipSuccess) {
+                    release(s);
+                    return hip_fail(e, "hipEventCreate");
+                }
             }
         }
-    }
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) {
-        release(s);
-        return hip_fail(e, "hipStreamSynchronize");
-    }
-    *out = s;
-    return ADAM_OK;
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess) {
+            release(s);
+            return hip_fail(e, "hipStreamSynchronize");
+        }
+        *out = s;
+        return ADAM_OK;
+    });
 }
 
 void adam_state_destroy(adam_state *s) { release(s); }
@@ -384,133 +411,139 @@ bool get(const uint8_t *base, int64_t n, int64_t &off, T &v) {
 extern "C" {
 
 int64_t adam_state_serialized_bytes(const adam_state *s) {
-    if (!s) return fail(ADAM_EINVAL, "state is NULL");
-    int64_t n = header_bytes(s->n_tensors);
-    for (int32_t b : buffers_of(s->layout)) n += 16 + align8(buffer_of(s, b).bytes);
-    return n + 16;
+    return guarded([&]() -> int64_t {
+        if (!s) return fail(ADAM_EINVAL, "state is NULL");
+        int64_t n = header_bytes(s->n_tensors);
+        for (int32_t b : buffers_of(s->layout)) n += 16 + align8(buffer_of(s, b).bytes);
+        return n + 16;
+    });
 }
 
 int adam_state_save(adam_state *s, void *dst, int64_t nbytes, void *hip_stream) {
-    if (!s || !dst) return fail(ADAM_EINVAL, "state or destination is NULL");
-    const int64_t need = adam_state_serialized_bytes(s);
-    if (nbytes != need)
-        return fail(ADAM_EINVAL, "nbytes " + std::to_string(nbytes) + " != serialized size " + std::to_string(need));
-    uint8_t *out = static_cast<uint8_t *>(dst);
-    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-    int64_t off = 0;
-    std::memcpy(out, kMagic, 8);
-    off = 8;
-    put<uint32_t>(out, off, kFormatVersion);
-    put<uint32_t>(out, off, (uint32_t)header_bytes(s->n_tensors));
-    put<int32_t>(out, off, s->layout.storage);
-    put<int32_t>(out, off, s->layout.grad_dtype);
-    put<int32_t>(out, off, s->layout.block_size);
-    put<uint32_t>(out, off, s->layout.options);
-    put<int32_t>(out, off, s->n_tensors);
-    put<uint32_t>(out, off, 0u);
-    for (int32_t k = 0; k < s->n_tensors; ++k) put<int64_t>(out, off, s->numels[k]);
-    const std::vector<int32_t> bufs = buffers_of(s->layout);
-    hipError_t e;
-    for (int32_t b : bufs) {
-        const BufferView v = buffer_of(s, b);
-        put<uint32_t>(out, off, (uint32_t)b);
+    return guarded([&]() -> int {
+        if (!s || !dst) return fail(ADAM_EINVAL, "state or destination is NULL");
+        const int64_t need = adam_state_serialized_bytes(s);
+        if (nbytes != need)
+            return fail(ADAM_EINVAL, "nbytes " + std::to_string(nbytes) + " != serialized size " + std::to_string(need));
+        uint8_t *out = static_cast<uint8_t *>(dst);
+        hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+        int64_t off = 0;
+        std::memcpy(out, kMagic, 8);
+        off = 8;
+        put<uint32_t>(out, off, kFormatVersion);
+        put<uint32_t>(out, off, (uint32_t)header_bytes(s->n_tensors));
+        put<int32_t>(out, off, s->layout.storage);
+        put<int32_t>(out, off, s->layout.grad_dtype);
+        put<int32_t>(out, off, s->layout.block_size);
+        put<uint32_t>(out, off, s->layout.options);
+        put<int32_t>(out, off, s->n_tensors);
         put<uint32_t>(out, off, 0u);
-        put<uint64_t>(out, off, (uint64_t)v.bytes);
-        if (v.bytes > 0 &&
-            (e = hipMemcpyAsync(out + off, v.ptr, (size_t)v.bytes, hipMemcpyDeviceToHost, stream)) != hipSuccess)
-            return hip_fail(e, "state copy to host");
-        std::memset(out + off + v.bytes, 0, (size_t)(align8(v.bytes) - v.bytes));
-        off += align8(v.bytes);
-    }
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    put<uint32_t>(out, off, kEndMarker);
-    put<uint32_t>(out, off, (uint32_t)bufs.size());
-    const uint64_t h = stream_hash(out, off);
-    put<uint64_t>(out, off, h);
-    return ADAM_OK;
+        for (int32_t k = 0; k < s->n_tensors; ++k) put<int64_t>(out, off, s->numels[k]);
+        const std::vector<int32_t> bufs = buffers_of(s->layout);
+        hipError_t e;
+        for (int32_t b : bufs) {
+            const BufferView v = buffer_of(s, b);
+            put<uint32_t>(out, off, (uint32_t)b);
+            put<uint32_t>(out, off, 0u);
+            put<uint64_t>(out, off, (uint64_t)v.bytes);
+            if (v.bytes > 0 &&
+                (e = hipMemcpyAsync(out + off, v.ptr, (size_t)v.bytes, hipMemcpyDeviceToHost, stream)) != hipSuccess)
+                return hip_fail(e, "state copy to host");
+            std::memset(out + off + v.bytes, 0, (size_t)(align8(v.bytes) - v.bytes));
+            off += align8(v.bytes);
+        }
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+        put<uint32_t>(out, off, kEndMarker);
+        put<uint32_t>(out, off, (uint32_t)bufs.size());
+        const uint64_t h = stream_hash(out, off);
+        put<uint64_t>(out, off, h);
+        return ADAM_OK;
+    });
 }
 
 int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip_stream) {
-    if (!out || !src) return fail(ADAM_EINVAL, "out or source is NULL");
-    *out = nullptr;
-    const uint8_t *in = static_cast<const uint8_t *>(src);
-    int64_t off = 0;
-    if (nbytes < 40 + 16 || std::memcmp(in, kMagic, 8) != 0) return fail(ADAM_EINVAL, "not a serialized Adam state");
-    off = 8;
-    uint32_t version = 0, hbytes = 0, hzero = 1;
-    adam_layout lay{};
-    int32_t n_tensors = 0;
-    get(in, nbytes, off, version);
-    if (version != kFormatVersion) return fail(ADAM_EINVAL, "unsupported state format version " + std::to_string(version));
-    get(in, nbytes, off, hbytes);
-    get(in, nbytes, off, lay.storage);
-    get(in, nbytes, off, lay.grad_dtype);
-    get(in, nbytes, off, lay.block_size);
-    get(in, nbytes, off, lay.options);
-    get(in, nbytes, off, n_tensors);
-    get(in, nbytes, off, hzero);
-    if (n_tensors < 0 || hzero != 0 || (int64_t)hbytes != header_bytes(n_tensors) || (int64_t)hbytes > nbytes - 16)
-        return fail(ADAM_EINVAL, "corrupt state header");
-    int rc = check_layout(&lay);
-    if (rc) return rc;
-    std::vector<int64_t> numels(n_tensors);
-    for (int32_t k = 0; k < n_tensors; ++k) get(in, nbytes, off, numels[k]);
-    if ((rc = check_numels(n_tensors, numels.data()))) return rc;
-    // the trailer and checksum cover everything before the checksum itself
-    if (nbytes % 8 != 0) return fail(ADAM_EINVAL, "serialized state size is not a multiple of 8");
-    uint64_t want_hash = 0;
-    std::memcpy(&want_hash, in + nbytes - 8, 8);
-    if (stream_hash(in, nbytes - 8) != want_hash) return fail(ADAM_EINVAL, "serialized state checksum mismatch");
-    // records: exactly the layout's buffers, in order, with the sizes it implies
-    const std::vector<int32_t> bufs = buffers_of(lay);
-    int64_t padded = 0, nblocks = 0;
-    for (int64_t n : numels) {
-        padded += pad16(n);
-        nblocks += blocks_of(n);
-    }
-    std::vector<std::pair<int64_t, int64_t>> payload;  // (offset, bytes) per record
-    for (int32_t b : bufs) {
-        uint32_t id = 0, zero = 1;
-        uint64_t len = 0;
-        if (!get(in, nbytes, off, id) || !get(in, nbytes, off, zero) || !get(in, nbytes, off, len))
-            return fail(ADAM_EINVAL, "truncated serialized state");
-        int64_t expect = 0;
-        switch (b) {
-        case ADAM_BUF_M_CODES: case ADAM_BUF_V_CODES: case ADAM_BUF_VMAX_CODES: expect = padded; break;
-        case ADAM_BUF_M_SCALE: case ADAM_BUF_V_SCALE: case ADAM_BUF_VMAX_SCALE: expect = 4 * nblocks; break;
-        case ADAM_BUF_M_BF16: case ADAM_BUF_V_BF16: case ADAM_BUF_VMAX_BF16: expect = 2 * padded; break;
-        default: expect = 4 * padded; break;
+    return guarded([&]() -> int {
+        if (!out || !src) return fail(ADAM_EINVAL, "out or source is NULL");
+        *out = nullptr;
+        const uint8_t *in = static_cast<const uint8_t *>(src);
+        int64_t off = 0;
+        if (nbytes < 40 + 16 || std::memcmp(in, kMagic, 8) != 0) return fail(ADAM_EINVAL, "not a serialized Adam state");
+        off = 8;
+        uint32_t version = 0, hbytes = 0, hzero = 1;
+        adam_layout lay{};
+        int32_t n_tensors = 0;
+        get(in, nbytes, off, version);
+        if (version != kFormatVersion) return fail(ADAM_EINVAL, "unsupported state format version " + std::to_string(version));
+        get(in, nbytes, off, hbytes);
+        get(in, nbytes, off, lay.storage);
+        get(in, nbytes, off, lay.grad_dtype);
+        get(in, nbytes, off, lay.block_size);
+        get(in, nbytes, off, lay.options);
+        get(in, nbytes, off, n_tensors);
+        get(in, nbytes, off, hzero);
+        if (n_tensors < 0 || hzero != 0 || (int64_t)hbytes != header_bytes(n_tensors) || (int64_t)hbytes > nbytes - 16)
+            return fail(ADAM_EINVAL, "corrupt state header");
+        int rc = check_layout(&lay);
+        if (rc) return rc;
+        std::vector<int64_t> numels(n_tensors);
+        for (int32_t k = 0; k < n_tensors; ++k) get(in, nbytes, off, numels[k]);
+        if ((rc = check_numels(n_tensors, numels.data()))) return rc;
+        // the trailer and checksum cover everything before the checksum itself
+        if (nbytes % 8 != 0) return fail(ADAM_EINVAL, "serialized state size is not a multiple of 8");
+        uint64_t want_hash = 0;
+        std::memcpy(&want_hash, in + nbytes - 8, 8);
+        if (stream_hash(in, nbytes - 8) != want_hash) return fail(ADAM_EINVAL, "serialized state checksum mismatch");
+        // records: exactly the layout's buffers, in order, with the sizes it implies
+        const std::vector<int32_t> bufs = buffers_of(lay);
+        int64_t padded = 0, nblocks = 0;
+        for (int64_t n : numels) {
+            padded += pad16(n);
+            nblocks += blocks_of(n);
         }
-        if ((int32_t)id != b || zero != 0 || (int64_t)len != expect)
-            return fail(ADAM_EINVAL, "state record " + std::to_string(b) + " missing, out of order or of the wrong size");
-        if (off + align8((int64_t)len) > nbytes - 16) return fail(ADAM_EINVAL, "truncated serialized state");
-        payload.emplace_back(off, (int64_t)len);
-        off += align8((int64_t)len);
-    }
-    uint32_t end = 0, count = 0;
-    get(in, nbytes, off, end);
-    get(in, nbytes, off, count);
-    if (end != kEndMarker || count != bufs.size() || off != nbytes - 8)
-        return fail(ADAM_EINVAL, "corrupt serialized state trailer");
+        std::vector<std::pair<int64_t, int64_t>> payload;  // (offset, bytes) per record
+        for (int32_t b : bufs) {
+            uint32_t id = 0, zero = 1;
+            uint64_t len = 0;
+            if (!get(in, nbytes, off, id) || !get(in, nbytes, off, zero) || !get(in, nbytes, off, len))
+                return fail(ADAM_EINVAL, "truncated serialized state");
+            int64_t expect = 0;
+            switch (b) {
+            case ADAM_BUF_M_CODES: case ADAM_BUF_V_CODES: case ADAM_BUF_VMAX_CODES: expect = padded; break;
+            case ADAM_BUF_M_SCALE: case ADAM_BUF_V_SCALE: case ADAM_BUF_VMAX_SCALE: expect = 4 * nblocks; break;
+            case ADAM_BUF_M_BF16: case ADAM_BUF_V_BF16: case ADAM_BUF_VMAX_BF16: expect = 2 * padded; break;
+            default: expect = 4 * padded; break;
+            }
+            if ((int32_t)id != b || zero != 0 || (int64_t)len != expect)
+                return fail(ADAM_EINVAL, "state record " + std::to_string(b) + " missing, out of order or of the wrong size");
+            if (off + align8((int64_t)len) > nbytes - 16) return fail(ADAM_EINVAL, "truncated serialized state");
+            payload.emplace_back(off, (int64_t)len);
+            off += align8((int64_t)len);
+        }
+        uint32_t end = 0, count = 0;
+        get(in, nbytes, off, end);
+        get(in, nbytes, off, count);
+        if (end != kEndMarker || count != bufs.size() || off != nbytes - 8)
+            return fail(ADAM_EINVAL, "corrupt serialized state trailer");
 
-    adam_state *s = nullptr;
-    if ((rc = adam_state_create(&s, n_tensors, numels.data(), &lay, hip_stream))) return rc;
-    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-    hipError_t e;
-    for (size_t i = 0; i < bufs.size(); ++i) {
-        const BufferView v = buffer_of(s, bufs[i]);
-        if (v.bytes > 0 && (e = hipMemcpyAsync(v.ptr, in + payload[i].first, (size_t)v.bytes,
-                                               hipMemcpyHostToDevice, stream)) != hipSuccess) {
-            release(s);
-            return hip_fail(e, "state copy to device");
+        adam_state *s = nullptr;
+        if ((rc = adam_state_create(&s, n_tensors, numels.data(), &lay, hip_stream))) return rc;
+        hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+        hipError_t e;
+        for (size_t i = 0; i < bufs.size(); ++i) {
+            const BufferView v = buffer_of(s, bufs[i]);
+            if (v.bytes > 0 && (e = hipMemcpyAsync(v.ptr, in + payload[i].first, (size_t)v.bytes,
+                                                   hipMemcpyHostToDevice, stream)) != hipSuccess) {
+                release(s);
+                return hip_fail(e, "state copy to device");
+            }
         }
-    }
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) {
-        release(s);
-        return hip_fail(e, "hipStreamSynchronize");
-    }
-    *out = s;
-    return ADAM_OK;
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess) {
+            release(s);
+            return hip_fail(e, "hipStreamSynchronize");
+        }
+        *out = s;
+        return ADAM_OK;
+    });
 }
 
 int32_t adam_state_describe(const adam_state *s, adam_layout *layout, int64_t *numels, int32_t max_tensors) {
@@ -553,102 +586,104 @@ int adam_state_write(adam_state *s, int32_t which, const void *src, int64_t nbyt
 
 int adam_step(adam_state *s, float *const *params, const void *const *grads, const adam_hparams *hp,
               const adam_layout *expect, void *hip_stream) {
-    if (!s) return fail(ADAM_EINVAL, "state is NULL");
-    if (!expect) return fail(ADAM_EINVAL, "expected layout is NULL");
-    if (expect->storage != s->layout.storage || expect->grad_dtype != s->layout.grad_dtype ||
-        expect->block_size != s->layout.block_size || expect->options != s->layout.options)
-        return fail(ADAM_EMODE, "layout differs from the one the state was created with");
-    int rc = check_hparams(hp, s->layout.storage);
-    if (rc) return rc;
-    if (s->n_tensors > 0 && (!params || !grads)) return fail(ADAM_EINVAL, "params or grads is NULL");
-    for (int32_t k = 0; k < s->n_tensors; ++k) {
-        if (s->numels[k] == 0) continue;
-        if (!params[k] || !grads[k]) return fail(ADAM_EINVAL, "NULL pointer for tensor " + std::to_string(k));
-        if ((reinterpret_cast<uintptr_t>(params[k]) | reinterpret_cast<uintptr_t>(grads[k])) & 15u)
-            return fail(ADAM_EALIGN, "tensor " + std::to_string(k) + " is not 16-byte aligned");
-    }
-    if (s->nblocks == 0) return ADAM_OK;
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if (dev != s->device)
-        return fail(ADAM_EINVAL, "state lives on device " + std::to_string(s->device) + ", current is " +
-                                     std::to_string(dev));
-    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-
-    // the device pointer table holding these pointers (uploading it if new)
-    int slot = -1;
-    for (int i = 0; i < kTableSlots && slot < 0; ++i) {
-        const TableSlot &ts = s->tables[i];
-        if (!ts.valid) continue;
-        bool same = true;
-        for (int32_t k = 0; k < s->n_tensors && same; ++k)
-            same = ts.ptrs[k].p == params[k] && ts.ptrs[k].g == grads[k];
-        if (same) slot = i;
-    }
-    if (slot < 0) {
-        slot = 0;  // least recently used (or never used) table
-        for (int i = 1; i < kTableSlots; ++i)
-            if (!s->tables[i].valid || (s->tables[slot].valid && s->tables[i].last_use < s->tables[slot].last_use))
-                slot = i;
-        TableSlot &ts = s->tables[slot];
-        const int st = s->next_stage;
-        s->next_stage = (st + 1) % kStageSlots;
-        if (s->stage_pending[st]) {  // the ring wrapped onto a copy still queued
-            if ((e = hipEventSynchronize(s->stage_done[st])) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-            s->stage_pending[st] = false;
+    return guarded([&]() -> int {
+        if (!s) return fail(ADAM_EINVAL, "state is NULL");
+        if (!expect) return fail(ADAM_EINVAL, "expected layout is NULL");
+        if (expect->storage != s->layout.storage || expect->grad_dtype != s->layout.grad_dtype ||
+            expect->block_size != s->layout.block_size || expect->options != s->layout.options)
+            return fail(ADAM_EMODE, "layout differs from the one the state was created with");
+        int rc = check_hparams(hp, s->layout.storage);
+        if (rc) return rc;
+        if (s->n_tensors > 0 && (!params || !grads)) return fail(ADAM_EINVAL, "params or grads is NULL");
+        for (int32_t k = 0; k < s->n_tensors; ++k) {
+            if (s->numels[k] == 0) continue;
+            if (!params[k] || !grads[k]) return fail(ADAM_EINVAL, "NULL pointer for tensor " + std::to_string(k));
+            if ((reinterpret_cast<uintptr_t>(params[k]) | reinterpret_cast<uintptr_t>(grads[k])) & 15u)
+                return fail(ADAM_EALIGN, "tensor " + std::to_string(k) + " is not 16-byte aligned");
         }
-        ts.valid = false;
-        ts.ptrs.resize(s->n_tensors);
-        for (int32_t k = 0; k < s->n_tensors; ++k) ts.ptrs[k] = TensorRef{params[k], grads[k]};
-        std::memcpy(s->stage[st], ts.ptrs.data(), s->n_tensors * sizeof(TensorRef));
-        // stream order puts this copy after every earlier kernel that reads ts.dev
-        e = hipMemcpyAsync(ts.dev, s->stage[st], s->n_tensors * sizeof(TensorRef), hipMemcpyHostToDevice, stream);
-        if (e != hipSuccess) return hip_fail(e, "pointer table upload");
-        if ((e = hipEventRecord(s->stage_done[st], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        s->stage_pending[st] = true;
-        ts.valid = true;
-    }
-    s->tables[slot].last_use = ++s->table_clock;
+        if (s->nblocks == 0) return ADAM_OK;
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        if (dev != s->device)
+            return fail(ADAM_EINVAL, "state lives on device " + std::to_string(s->device) + ", current is " +
+                                         std::to_string(dev));
+        hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
 
-    // host scalars: fp64, each rounded once to fp32
-    const double b1 = hp->beta1, b2 = hp->beta2;
-    const double bc1 = 1.0 - std::pow(b1, (double)hp->t);
-    const double bc2 = 1.0 - std::pow(b2, (double)hp->t);
-    const bool decoupled = (hp->flags & ADAM_F_DECOUPLED_WD) != 0;
-    StepArgs a{};
-    a.desc = s->d_desc;
-    a.tensors = s->tables[slot].dev;
-    a.m_state = s->m;
-    a.v_state = s->v;
-    a.m_scale = s->m_scale;
-    a.v_scale = s->v_scale;
-    a.w_state = s->w;
-    a.w_scale = s->w_scale;
-    a.step = (float)((double)hp->lr / bc1);
-    a.ibc2 = (float)(1.0 / std::sqrt(bc2));
-    a.decay = decoupled ? (float)(1.0 - (double)hp->lr * (double)hp->weight_decay) : 1.0f;
-    a.omb1 = (float)(1.0 - b1);
-    a.omb2 = (float)(1.0 - b2);
-    a.beta1 = hp->beta1;
-    a.beta2 = hp->beta2;
-    a.eps = hp->eps;
-    a.wd = hp->weight_decay;
-    a.l2 = decoupled ? 0u : 1u;
-    a.fast_ok = (hp->eps >= 0x1p-40f && hp->eps <= 0x1p20f) ? 1u : 0u;
-    a.pfrac = (double)hp->percentile / 100.0;
-    a.seed_lo = (uint32_t)hp->seed;
-    a.seed_hi = (uint32_t)(hp->seed >> 32);
-    a.t_lo = (uint32_t)(uint64_t)hp->t;
-    a.t_hi = (uint32_t)((uint64_t)hp->t >> 32);
+        // the device pointer table holding these pointers (uploading it if new)
+        int slot = -1;
+        for (int i = 0; i < kTableSlots && slot < 0; ++i) {
+            const TableSlot &ts = s->tables[i];
+            if (!ts.valid) continue;
+            bool same = true;
+            for (int32_t k = 0; k < s->n_tensors && same; ++k)
+                same = ts.ptrs[k].p == params[k] && ts.ptrs[k].g == grads[k];
+            if (same) slot = i;
+        }
+        if (slot < 0) {
+            slot = 0;  // least recently used (or never used) table
+            for (int i = 1; i < kTableSlots; ++i)
+                if (!s->tables[i].valid || (s->tables[slot].valid && s->tables[i].last_use < s->tables[slot].last_use))
+                    slot = i;
+            TableSlot &ts = s->tables[slot];
+            const int st = s->next_stage;
+            s->next_stage = (st + 1) % kStageSlots;
+            if (s->stage_pending[st]) {  // the ring wrapped onto a copy still queued
+                if ((e = hipEventSynchronize(s->stage_done[st])) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+                s->stage_pending[st] = false;
+            }
+            ts.valid = false;
+            ts.ptrs.resize(s->n_tensors);
+            for (int32_t k = 0; k < s->n_tensors; ++k) ts.ptrs[k] = TensorRef{params[k], grads[k]};
+            std::memcpy(s->stage[st], ts.ptrs.data(), s->n_tensors * sizeof(TensorRef));
+            // stream order puts this copy after every earlier kernel that reads ts.dev
+            e = hipMemcpyAsync(ts.dev, s->stage[st], s->n_tensors * sizeof(TensorRef), hipMemcpyHostToDevice, stream);
+            if (e != hipSuccess) return hip_fail(e, "pointer table upload");
+            if ((e = hipEventRecord(s->stage_done[st], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            s->stage_pending[st] = true;
+            ts.valid = true;
+        }
+        s->tables[slot].last_use = ++s->table_clock;
 
-    a.n_full = (uint32_t)s->n_full;
-    a.n_all = (uint32_t)s->nblocks;
-    Variant v{s->layout.storage, s->layout.grad_dtype == ADAM_GRAD_BF16, (hp->flags & ADAM_F_STOCHASTIC) != 0,
-              (hp->flags & ADAM_F_PERCENTILE) != 0, (hp->flags & ADAM_F_STATIC_SCALES) != 0,
-              amsgrad(s->layout)};
-    if ((e = launch_step(v, a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
-    return ADAM_OK;
+        // host scalars: fp64, each rounded once to fp32
+        const double b1 = hp->beta1, b2 = hp->beta2;
+        const double bc1 = 1.0 - std::pow(b1, (double)hp->t);
+        const double bc2 = 1.0 - std::pow(b2, (double)hp->t);
+        const bool decoupled = (hp->flags & ADAM_F_DECOUPLED_WD) != 0;
+        StepArgs a{};
+        a.desc = s->d_desc;
+        a.tensors = s->tables[slot].dev;
+        a.m_state = s->m;
+        a.v_state = s->v;
+        a.m_scale = s->m_scale;
+        a.v_scale = s->v_scale;
+        a.w_state = s->w;
+        a.w_scale = s->w_scale;
+        a.step = (float)((double)hp->lr / bc1);
+        a.ibc2 = (float)(1.0 / std::sqrt(bc2));
+        a.decay = decoupled ? (float)(1.0 - (double)hp->lr * (double)hp->weight_decay) : 1.0f;
+        a.omb1 = (float)(1.0 - b1);
+        a.omb2 = (float)(1.0 - b2);
+        a.beta1 = hp->beta1;
+        a.beta2 = hp->beta2;
+        a.eps = hp->eps;
+        a.wd = hp->weight_decay;
+        a.l2 = decoupled ? 0u : 1u;
+        a.fast_ok = (hp->eps >= 0x1p-40f && hp->eps <= 0x1p20f) ? 1u : 0u;
+        a.pfrac = (double)hp->percentile / 100.0;
+        a.seed_lo = (uint32_t)hp->seed;
+        a.seed_hi = (uint32_t)(hp->seed >> 32);
+        a.t_lo = (uint32_t)(uint64_t)hp->t;
+        a.t_hi = (uint32_t)((uint64_t)hp->t >> 32);
+
+        a.n_full = (uint32_t)s->n_full;
+        a.n_all = (uint32_t)s->nblocks;
+        Variant v{s->layout.storage, s->layout.grad_dtype == ADAM_GRAD_BF16, (hp->flags & ADAM_F_STOCHASTIC) != 0,
+                  (hp->flags & ADAM_F_PERCENTILE) != 0, (hp->flags & ADAM_F_STATIC_SCALES) != 0,
+                  amsgrad(s->layout)};
+        if ((e = launch_step(v, a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
+        return ADAM_OK;
+    });
 }
 
 }  // extern "C"

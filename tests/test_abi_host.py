@@ -106,6 +106,18 @@ def test_create_rejects_bad_arguments_before_any_device_call():
     assert h.value is None
 
 
+def test_create_rejects_an_oversized_state_before_building_it():
+    # 17 tensors of 2^32 - 1 elements pass the per-tensor limit but exceed
+    # 2^36 padded state entries in total: refused up front (no host tables
+    # built, no device call)
+    lib = ma.library()
+    n, arr = B._numels([2 ** 32 - 1] * 17)
+    h = ctypes.c_void_p()
+    lay = B._layout("q8", "bf16")
+    assert lib.adam_state_create(ctypes.byref(h), n, arr, ctypes.byref(lay), None) == -1
+    assert "too large" in ma.adam_last_error() and h.value is None
+
+
 def test_step_and_buffer_calls_reject_null_state():
     lib = ma.library()
     hp = B.adam_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 100.0, 1, 1, 0, 0)
