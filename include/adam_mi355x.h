@@ -55,7 +55,9 @@
  * enqueued on the caller's HIP stream (hipStream_t passed as void*; NULL is
  * the null stream); argument errors are reported synchronously before any
  * device work.  adam_last_error() returns a thread-local message for the
- * last failing call on the calling thread.
+ * last failing call on the calling thread.  A host memory allocation that
+ * fails inside any call returns ADAM_ENOMEM (no C++ exception crosses the
+ * interface).
  */
 #ifndef ADAM_MI355X_H
 #define ADAM_MI355X_H
