@@ -38,9 +38,11 @@
  * code q decodes to (q * fl(1/qmax)) * A with qmax = 127 (m, int8, -128
  * never produced) or 255 (v, uint8); encoding rounds |x| * fl(qmax/A) to
  * nearest-even (or stochastically: up iff u < frac with u a 16-bit draw of
- * Philox4x32-10, key = seed, counter = (flat index / 4, t), word = flat
- * index mod 4, low half for m and high half for v; the AMSGrad maximum
- * takes the low half of the word at counter (flat index / 4 + 2^63, t)) and
+ * Philox4x32-10, key = seed, counter = (draw index / 4, t), word = draw
+ * index mod 4 -- the draw index being the flat index unless set otherwise
+ * (adam_state_set_draw_index) -- low half for m and high half for v; the
+ * AMSGrad maximum takes the low half of the word at counter (draw index / 4
+ * + 2^63, t)) and
  * pins |x| >= A to qmax; a block with A < 2^-112 stores zero codes and
  * scale 0.  The AMSGrad maximum is stored as v is: bf16, or uint8 codes
  * with their own per-block scale.
@@ -208,9 +210,10 @@ int adam_state_write(adam_state *s, int32_t which, const void *src, int64_t nbyt
  * marker per moment so that a reader never assumes a buffer the writer did
  * not store.  The serialized form is a self-describing little-endian byte
  * stream in host memory:
- *   header   "MEAMSTAT", u32 version (2), u32 header bytes (40 + 8*n),
+ *   header   "MEAMSTAT", u32 version (2), u32 header bytes (40 + 16*n),
  *            i32 storage, i32 grad_dtype, i32 block_size, u32 options,
- *            i32 n_tensors, u32 0, i64 numels[n_tensors]
+ *            i32 n_tensors, u32 0, i64 numels[n_tensors],
+ *            i64 draw_index[n_tensors] (adam_state_set_draw_index)
  *   records  one per state buffer the layout has (enum adam_buffer order):
  *            u32 buffer id, u32 0, u64 byte count, the bytes, zero padding
  *            to a multiple of 8
@@ -222,8 +225,8 @@ int adam_state_write(adam_state *s, int32_t which, const void *src, int64_t nbyt
  * the serialized size); the device copies are ordered on hip_stream after
  * earlier work on the state, and the call returns once dst is complete.
  * adam_state_load: validates the whole stream on the host (magic, version,
- * layout, numels, the exact set and sizes of the records, trailer and
- * checksum) before any device call, then creates a state on the current
+ * layout, numels, draw indices, the exact set and sizes of the records,
+ * trailer and checksum) before any device call, then creates a state on the current
  * device holding exactly the saved contents (free with adam_state_destroy).
  * A resumed run is bit-identical to an uninterrupted one.
  * Errors: EINVAL (NULL pointers, size mismatch, any validation failure),
@@ -232,6 +235,27 @@ int adam_state_write(adam_state *s, int32_t which, const void *src, int64_t nbyt
 int64_t adam_state_serialized_bytes(const adam_state *s);
 int adam_state_save(adam_state *s, void *dst, int64_t nbytes, void *hip_stream);
 int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip_stream);
+
+/*
+ * Stochastic-rounding draw index of each tensor's element 0.  The draws of
+ * an element come from the Philox counter of its draw index (see the
+ * numerics above); by default that is the element's flat index in this
+ * state.  A state that holds a shard of a larger parameter set (ZeRO-1:
+ * block-aligned slices of tensors on several GPUs) sets, for each slice,
+ * the flat index its first element has in the unsharded state, so that the
+ * shards together draw exactly the unsharded state's stream.  The indices
+ * are part of the state and of its checkpoint.
+ * adam_state_set_draw_index: first_index[k] for k < n_tensors, each a
+ * multiple of 16 with first_index[k] + pad16(numel_k) <= 2^62; uploaded on
+ * hip_stream, ordered after earlier steps on it, and the call returns once
+ * done.  Errors: EINVAL (NULL state, NULL array with tensors, an index out
+ * of range), EDEVICE.
+ * adam_state_get_draw_index (pure host): the first min(n_tensors,
+ * max_tensors) indices into first_index; returns the tensor count, or < 0
+ * on a NULL state (or NULL array with max_tensors > 0).
+ */
+int adam_state_set_draw_index(adam_state *s, const int64_t *first_index, void *hip_stream);
+int32_t adam_state_get_draw_index(const adam_state *s, int64_t *first_index, int32_t max_tensors);
 
 /* Describes a state (pure host): its layout and tensor count, and the
    first min(n_tensors, max_tensors) element counts into numels (which may

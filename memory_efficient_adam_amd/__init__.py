@@ -21,10 +21,12 @@ from ._binding import (  # noqa: F401
     adam_state_create,
     adam_state_describe,
     adam_state_destroy,
+    adam_state_get_draw_index,
     adam_state_load,
     adam_state_read,
     adam_state_save,
     adam_state_serialized_bytes,
+    adam_state_set_draw_index,
     adam_state_write,
     adam_step,
     library,

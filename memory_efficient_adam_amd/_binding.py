@@ -74,6 +74,10 @@ def library():
     L.adam_state_save.restype = ctypes.c_int
     L.adam_state_load.argtypes = [ctypes.POINTER(vp), vp, ctypes.c_int64, vp]
     L.adam_state_load.restype = ctypes.c_int
+    L.adam_state_set_draw_index.argtypes = [vp, i64p, vp]
+    L.adam_state_set_draw_index.restype = ctypes.c_int
+    L.adam_state_get_draw_index.argtypes = [vp, i64p, ctypes.c_int32]
+    L.adam_state_get_draw_index.restype = ctypes.c_int32
     L.adam_state_destroy.argtypes = [vp]
     L.adam_state_destroy.restype = None
     L.adam_last_error.argtypes = []
@@ -229,6 +233,24 @@ def adam_state_describe(state):
     arr = (ctypes.c_int64 * max(n, 1))()
     library().adam_state_describe(state.handle, ctypes.byref(lay), arr, n)
     return lay, [int(arr[i]) for i in range(n)]
+
+
+def adam_state_set_draw_index(state, first_index, stream=None):
+    """Per tensor: the stochastic-rounding draw index of element 0 (e.g. a
+    shard slice's flat index in the unsharded state)."""
+    n, arr = _numels(first_index)
+    if n != len(state.numels):
+        raise ValueError(f"expected {len(state.numels)} draw indices")
+    _check(library().adam_state_set_draw_index(state.handle, arr, _stream(stream)))
+
+
+def adam_state_get_draw_index(state):
+    n = len(state.numels)
+    arr = (ctypes.c_int64 * max(n, 1))()
+    rc = library().adam_state_get_draw_index(state.handle, arr, n)
+    if rc < 0:
+        raise AdamError(int(rc), adam_last_error())
+    return [int(arr[i]) for i in range(n)]
 
 
 def adam_state_serialized_bytes(state):

@@ -42,6 +42,7 @@ struct StepArgs {
     void *v_state;   // bf16 / uint8 codes
     float *m_scale;  // per block (Q8)
     float *v_scale;  // per block (Q8, Q8_V_ONLY)
+    const uint64_t *draw_first;  // per tensor: stochastic-rounding draw index of element 0
     void *w_state;   // AMSGrad running max of v: bf16 / uint8 codes (else NULL)
     float *w_scale;  // its per-block scale (8-bit storage with AMSGrad)
     float step;      // lr / (1 - beta1^t)

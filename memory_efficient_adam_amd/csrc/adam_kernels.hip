@@ -258,6 +258,7 @@ __device__ __forceinline__ uint32_t code_magnitude(float a, float A, float r, ui
 // Scalars of one block: where its data lives and its stored scales.
 struct BlockCtx {
     uint64_t gidx;   // flat state index of the block's first element
+    uint64_t didx;   // stochastic-rounding draw index of the block's first element
     float *p;        // the block's params
     const void *g;   // the block's grads
     uint32_t n;      // live elements (1..2048)
@@ -265,12 +266,13 @@ struct BlockCtx {
     uint32_t slot;   // scale slot
 };
 
-// The descriptor and pointer tables do not change during a launch: reading
+// The descriptor, pointer and draw-index tables do not change during a launch: reading
 // them through the constant address space lets them be scalar loads even
 // after the kernel's own stores (a generic load there would be a vector load
 // whose wait also drains every prefetched data load).
 typedef const __attribute__((address_space(4))) BlockDesc *ConstDescPtr;
 typedef const __attribute__((address_space(4))) TensorRef *ConstTensorPtr;
+typedef const __attribute__((address_space(4))) uint64_t *ConstU64Ptr;
 
 template <bool kGradBf16>
 __device__ __forceinline__ BlockCtx load_ctx(const StepArgs &a, uint32_t idx) {
@@ -280,6 +282,7 @@ __device__ __forceinline__ BlockCtx load_ctx(const StepArgs &a, uint32_t idx) {
     const size_t local = (size_t)(lb_n >> kBlockBits) * kBlock;
     BlockCtx c;
     c.gidx = (uint64_t)d->gidx16 * 16u;
+    c.didx = ((ConstU64Ptr)a.draw_first)[d->tensor] + local;
     c.p = tr->p + local;
     c.g = kGradBf16 ? (const void *)(reinterpret_cast<const uint16_t *>(tr->g) + local)
                     : (const void *)(reinterpret_cast<const float *>(tr->g) + local);
@@ -645,7 +648,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             const size_t s = c.gidx + e0;
             uint32_t rnd[4] = {0u, 0u, 0u, 0u}, rnd_w[4] = {0u, 0u, 0u, 0u};
             if constexpr (kSR) {
-                const uint64_t grp = s >> 2;
+                const uint64_t grp = (c.didx + e0) >> 2;  // draw index / 4
                 uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), a.t_lo, a.t_hi};
                 philox4x32_10(ctr, a.seed_lo, a.seed_hi);
                 rnd[0] = ctr[0]; rnd[1] = ctr[1]; rnd[2] = ctr[2]; rnd[3] = ctr[3];

@@ -39,6 +39,10 @@ struct adam_state {
     int64_t nblocks = 0;
     int64_t n_full = 0;   // blocks of 2048 elements (listed first)
     BlockDesc *d_desc = nullptr;
+    // per tensor: the stochastic-rounding draw index of element 0 (default:
+    // the tensor's own segment start in this state)
+    std::vector<int64_t> draw_first;
+    uint64_t *d_draw = nullptr;
     // Device copies of the caller's per-tensor {param, grad} pointer pairs.
     // A few recently used pointer sets stay resident, so a caller that
     // alternates between gradient buffers uploads nothing; a new set is
@@ -148,6 +152,21 @@ int hip_fail(hipError_t e, const char *what) {
     return fail(ADAM_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// draw indices stay below 2^62, so index / 4 never reaches bit 63 of the Philox
+// group counter, which the AMSGrad maximum's draws set
+constexpr int64_t kDrawIndexLimit = int64_t(1) << 62;
+
+// Draw indices must be multiples of 16 (a 4-element draw group never straddles
+// two tensors) and keep every element's index below 2^62.
+int check_draw_first(int32_t n_tensors, const int64_t *numels, const int64_t *first) {
+    if (n_tensors > 0 && !first) return fail(ADAM_EINVAL, "draw index array is NULL");
+    for (int32_t k = 0; k < n_tensors; ++k)
+        if (first[k] < 0 || first[k] % 16 != 0 || first[k] > kDrawIndexLimit - pad16(numels[k]))
+            return fail(ADAM_EINVAL, "draw index of tensor " + std::to_string(k) +
+                                         " must be a multiple of 16 in [0, 2^62 - padded size]");
+    return ADAM_OK;
+}
+
 void release(adam_state *s) {
     if (!s) return;
     if (s->device >= 0) {
@@ -161,6 +180,7 @@ void release(adam_state *s) {
         }
         for (int i = 0; i < kTableSlots; ++i) (void)hipFree(s->tables[i].dev);
         (void)hipFree(s->d_desc);
+        (void)hipFree(s->d_draw);
         (void)hipFree(s->m);
         (void)hipFree(s->v);
         (void)hipFree(s->m_scale);
@@ -262,6 +282,7 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
         std::vector<BlockDesc> desc, tails;
         try {
             s->numels.assign(numels, numels + n_tensors);
+            s->draw_first.resize(n_tensors);
             desc.reserve((size_t)total_blocks);
             int64_t slot = 0;
             for (int32_t k = 0; k < n_tensors; ++k) {
@@ -272,6 +293,7 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
                                       (uint32_t)((b << kBlockBits) | (len - 1)), (uint32_t)slot};
                     (len == kBlock ? desc : tails).push_back(d);
                 }
+                s->draw_first[k] = s->padded;
                 s->padded += pad16(n);
             }
             s->n_full = (int64_t)desc.size();
@@ -317,6 +339,17 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
             }
         }
         if (n_tensors > 0) {
+            if (hipMalloc((void **)&s->d_draw, (size_t)n_tensors * 8) != hipSuccess) {
+                (void)hipGetLastError();
+                release(s);
+                return fail(ADAM_ENOMEM, "hipMalloc of the draw-index table failed");
+            }
+            e = hipMemcpyAsync(s->d_draw, s->draw_first.data(), (size_t)n_tensors * 8, hipMemcpyHostToDevice,
+                               stream);
+            if (e != hipSuccess) {
+                release(s);
+                return hip_fail(e, "draw-index upload");
+            }
             const size_t tbytes = (size_t)n_tensors * sizeof(TensorRef);
             for (int i = 0; i < kTableSlots; ++i) {
                 if (hipMalloc((void **)&s->tables[i].dev, tbytes) != hipSuccess) {
@@ -392,7 +425,7 @@ std::vector<int32_t> buffers_of(const adam_layout &l) {
     return b;
 }
 
-int64_t header_bytes(int32_t n_tensors) { return 40 + 8 * (int64_t)n_tensors; }
+int64_t header_bytes(int32_t n_tensors) { return 40 + 16 * (int64_t)n_tensors; }
 
 template <class T>
 void put(uint8_t *base, int64_t &off, T v) {
@@ -439,6 +472,7 @@ int adam_state_save(adam_state *s, void *dst, int64_t nbytes, void *hip_stream) 
         put<int32_t>(out, off, s->n_tensors);
         put<uint32_t>(out, off, 0u);
         for (int32_t k = 0; k < s->n_tensors; ++k) put<int64_t>(out, off, s->numels[k]);
+        for (int32_t k = 0; k < s->n_tensors; ++k) put<int64_t>(out, off, s->draw_first[k]);
         const std::vector<int32_t> bufs = buffers_of(s->layout);
         hipError_t e;
         for (int32_t b : bufs) {
@@ -467,7 +501,8 @@ int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip
         *out = nullptr;
         const uint8_t *in = static_cast<const uint8_t *>(src);
         int64_t off = 0;
-        if (nbytes < 40 + 16 || std::memcmp(in, kMagic, 8) != 0) return fail(ADAM_EINVAL, "not a serialized Adam state");
+        if (nbytes < header_bytes(0) + 16 || std::memcmp(in, kMagic, 8) != 0)
+            return fail(ADAM_EINVAL, "not a serialized Adam state");
         off = 8;
         uint32_t version = 0, hbytes = 0, hzero = 1;
         adam_layout lay{};
@@ -488,6 +523,9 @@ int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip
         std::vector<int64_t> numels(n_tensors);
         for (int32_t k = 0; k < n_tensors; ++k) get(in, nbytes, off, numels[k]);
         if ((rc = check_numels(n_tensors, numels.data()))) return rc;
+        std::vector<int64_t> draw_first(n_tensors);
+        for (int32_t k = 0; k < n_tensors; ++k) get(in, nbytes, off, draw_first[k]);
+        if ((rc = check_draw_first(n_tensors, numels.data(), draw_first.data()))) return rc;
         // the trailer and checksum cover everything before the checksum itself
         if (nbytes % 8 != 0) return fail(ADAM_EINVAL, "serialized state size is not a multiple of 8");
         uint64_t want_hash = 0;
@@ -527,6 +565,10 @@ int adam_state_load(adam_state **out, const void *src, int64_t nbytes, void *hip
 
         adam_state *s = nullptr;
         if ((rc = adam_state_create(&s, n_tensors, numels.data(), &lay, hip_stream))) return rc;
+        if ((rc = adam_state_set_draw_index(s, draw_first.data(), hip_stream))) {
+            release(s);
+            return rc;
+        }
         hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
         hipError_t e;
         for (size_t i = 0; i < bufs.size(); ++i) {
@@ -551,6 +593,30 @@ int32_t adam_state_describe(const adam_state *s, adam_layout *layout, int64_t *n
     if (max_tensors > 0 && !numels) return fail(ADAM_EINVAL, "numels is NULL");
     *layout = s->layout;
     for (int32_t k = 0; k < s->n_tensors && k < max_tensors; ++k) numels[k] = s->numels[k];
+    return s->n_tensors;
+}
+
+int adam_state_set_draw_index(adam_state *s, const int64_t *first_index, void *hip_stream) {
+    return guarded([&]() -> int {
+        if (!s) return fail(ADAM_EINVAL, "state is NULL");
+        int rc = check_draw_first(s->n_tensors, s->numels.data(), first_index);
+        if (rc) return rc;
+        if (s->n_tensors == 0) return ADAM_OK;
+        hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+        std::copy(first_index, first_index + s->n_tensors, s->draw_first.begin());
+        // stream order puts the copy after every earlier step that read the table
+        hipError_t e = hipMemcpyAsync(s->d_draw, s->draw_first.data(), (size_t)s->n_tensors * 8,
+                                      hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "draw-index upload");
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+        return ADAM_OK;
+    });
+}
+
+int32_t adam_state_get_draw_index(const adam_state *s, int64_t *first_index, int32_t max_tensors) {
+    if (!s) return fail(ADAM_EINVAL, "state is NULL");
+    if (max_tensors > 0 && !first_index) return fail(ADAM_EINVAL, "first_index is NULL");
+    for (int32_t k = 0; k < s->n_tensors && k < max_tensors; ++k) first_index[k] = s->draw_first[k];
     return s->n_tensors;
 }
 
@@ -657,6 +723,7 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
         a.v_state = s->v;
         a.m_scale = s->m_scale;
         a.v_scale = s->v_scale;
+        a.draw_first = s->d_draw;
         a.w_state = s->w;
         a.w_scale = s->w_scale;
         a.step = (float)((double)hp->lr / bc1);

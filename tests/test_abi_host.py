@@ -147,14 +147,17 @@ def _stream_hash(b):
     return h ^ (h >> 32)
 
 
-def _serialized(numels, storage=2, records=None, version=2, options=0, pad_word=0):
+def _serialized(numels, storage=2, records=None, version=2, options=0, pad_word=0, draw=None):
     import struct
     pad16 = [(n + 15) // 16 * 16 for n in numels]
     blocks = sum(-(-n // 2048) for n in numels)
+    if draw is None:  # default draw indices: the segment starts
+        draw = [sum(pad16[:k]) for k in range(len(numels))]
     out = bytearray(b"MEAMSTAT")
-    out += struct.pack("<IIiiiIiI", version, 40 + 8 * len(numels), storage, 0, 2048, options,
+    out += struct.pack("<IIiiiIiI", version, 40 + 16 * len(numels), storage, 0, 2048, options,
                        len(numels), pad_word)
     out += struct.pack(f"<{len(numels)}q", *numels)
+    out += struct.pack(f"<{len(numels)}q", *draw)
     if records is None:
         P = sum(pad16)
         records = {2: [(0, P), (1, P), (2, 4 * blocks), (3, 4 * blocks)],
@@ -178,7 +181,8 @@ def _load_rc(buf):
 
 @pytest.mark.parametrize("mutate", ["magic", "version", "truncate", "checksum", "payload",
                                     "record_order", "record_size", "storage", "numel",
-                                    "options", "header_word", "amsgrad_records"])
+                                    "options", "header_word", "amsgrad_records",
+                                    "draw_unaligned", "draw_negative", "draw_too_large"])
 def test_load_rejects_malformed_streams_before_any_device_call(mutate):
     import struct
     numels = [5000, 17]
@@ -191,6 +195,12 @@ def test_load_rejects_malformed_streams_before_any_device_call(mutate):
         bad = _serialized(numels, options=2)
     elif mutate == "header_word":
         bad = _serialized(numels, pad_word=1)
+    elif mutate == "draw_unaligned":
+        bad = _serialized(numels, draw=[0, 5016])
+    elif mutate == "draw_negative":
+        bad = _serialized(numels, draw=[-16, 5008])
+    elif mutate == "draw_too_large":
+        bad = _serialized(numels, draw=[0, 2 ** 62 - 16])
     elif mutate == "amsgrad_records":
         # claims the AMSGrad option but holds only the plain buffers
         P = 5008 + 32
@@ -201,7 +211,7 @@ def test_load_rejects_malformed_streams_before_any_device_call(mutate):
         good[-1] ^= 0x40
         bad = bytes(good)
     elif mutate == "payload":
-        good[80] ^= 1  # inside the first record's bytes, checksum now stale
+        good[96] ^= 1  # inside the first record's bytes, checksum now stale
         bad = bytes(good)
     elif mutate == "record_order":
         P = 5008 + 32
@@ -221,11 +231,12 @@ def test_load_rejects_malformed_streams_before_any_device_call(mutate):
     assert rc == -1 and h is None, (mutate, ma.adam_last_error())
 
 
-@pytest.mark.parametrize("storage,options", [(2, 0), (1, 0), (3, 0), (2, 1), (1, 1), (3, 1)])
-def test_load_of_a_valid_stream_gets_past_validation(storage, options):
+@pytest.mark.parametrize("storage,options,draw", [(2, 0, None), (1, 0, None), (3, 0, None),
+                                                  (2, 1, None), (1, 1, None), (3, 1, [2 ** 40, 0])])
+def test_load_of_a_valid_stream_gets_past_validation(storage, options, draw):
     # a well-formed stream passes every host check; on a machine without a GPU
     # the first device call (state creation) is what fails
-    rc, h = _load_rc(_serialized([5000, 17], storage=storage, options=options))
+    rc, h = _load_rc(_serialized([5000, 17], storage=storage, options=options, draw=draw))
     if rc == 0:
         ma.library().adam_state_destroy(h)
     else:

@@ -11,6 +11,8 @@ gets and compares element by element (criteria in tests/parity.py):
     every tail block;
   * static scales (kept once set) on the ragged set, mixed with dynamic
     steps, and on the full-size Llama-7B set;
+  * ZeRO-1 shard states (block-aligned slices, draw indices set) against one
+    state over the whole set, bit for bit;
   * AMSGrad (running maximum of v) in every storage mode on the ragged set,
     on the full-size GPT-1.3B set with stochastic rounding, and through a
     checkpoint;
@@ -246,6 +248,109 @@ def test_random_configurations(i):
                 compare_buffer(nm, got[nm], want, hp["stochastic"], stats, f"t={t}")
     log(f"  {stats}")
     st.destroy()
+
+
+def _slices(shard):
+    """(tensor index, start, stop) of each slice named 't<k>[start:stop]'."""
+    out = []
+    for name, _ in shard:
+        base, rng = name.split("[")
+        lo, hi = (int(x) for x in rng.rstrip("]").split(":"))
+        out.append((int(base[1:]), lo, hi))
+    return out
+
+
+@pytest.mark.parametrize("storage,gdt,sr,ams,pct", [("q8", "bf16", True, False, None),
+                                                    ("q8_v_only", "f32", True, True, 99.9),
+                                                    ("bf16", "f32", False, True, None)])
+def test_zero1_shards_reproduce_the_unsharded_step(storage, gdt, sr, ams, pct):
+    # three states, each holding one rank's block-aligned slices of the set
+    # with their draw indices set to the slices' flat indices in the whole
+    # state, step to the same bits as one state over the whole set
+    sizes = [9001, 2048 * 3, 17, 4100, 6001, 2048]
+    shapes = [(f"t{k}", (n,)) for k, n in enumerate(sizes)]
+    log(f"ZeRO-1 shards x3 {storage} sr={sr} amsgrad={ams} pct={pct}")
+    seg = np.concatenate([[0], np.cumsum([oracle.pad16(n) for n in sizes])])
+    blk0 = np.concatenate([[0], np.cumsum([-(-n // 2048) for n in sizes])])
+    hp = dict(HP, stochastic=sr, percentile=pct, seed=2024)
+    p0 = workloads.host_params(41, sizes)
+    whole_p = [torch.from_numpy(x.copy()).cuda() for x in p0]
+    shard_p = [torch.from_numpy(x.copy()).cuda() for x in p0]
+    whole = ma.adam_state_create(sizes, storage, gdt, amsgrad=ams)
+    shards = []
+    for r in range(3):
+        sl = _slices(workloads.zero1_shard_shapes(shapes, r, 3))
+        st = ma.adam_state_create([b - a for _, a, b in sl], storage, gdt, amsgrad=ams)
+        ma.adam_state_set_draw_index(st, [int(seg[k]) + a for k, a, _ in sl])
+        assert ma.adam_state_get_draw_index(st) == [int(seg[k]) + a for k, a, _ in sl]
+        shards.append((sl, st))
+    for t in range(1, 5):
+        g = to_device_grads(workloads.host_grads(41, sizes, t, dtype=gdt), gdt)
+        ma.adam_step(whole, whole_p, g, t=t, **hp)
+        for sl, st in shards:
+            ma.adam_step(st, [shard_p[k][a:b] for k, a, b in sl], [g[k][a:b] for k, a, b in sl],
+                         t=t, **hp)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(whole_p, shard_p):
+        assert torch.equal(a_.view(torch.int32), b_.view(torch.int32))
+    want = read_state(whole)
+    for sl, st in shards:
+        got = read_state(st)
+        sseg, sblk = 0, 0
+        for k, a, b in sl:
+            for nm, w in want.items():
+                if nm.endswith("scale"):
+                    nb = -(-(b - a) // 2048)
+                    g0 = blk0[k] + a // 2048
+                    assert np.array_equal(got[nm][sblk:sblk + nb].view(np.uint32),
+                                          w[g0:g0 + nb].view(np.uint32)), (nm, k, a)
+                else:
+                    gv = got[nm][sseg:sseg + b - a]
+                    wv = w[seg[k] + a:seg[k] + b]
+                    assert np.array_equal(gv.view(np.uint8), wv.view(np.uint8)), (nm, k, a)
+            sseg += oracle.pad16(b - a)
+            sblk += -(-(b - a) // 2048)
+        st.destroy()
+    whole.destroy()
+
+
+def test_draw_index_validation_and_checkpoint():
+    numels = [5000, 17]
+    st = ma.adam_state_create(numels, "q8", "f32")
+    assert ma.adam_state_get_draw_index(st) == [0, 5008]
+    for bad in ([8, 5008], [-16, 5008], [0, 2 ** 62 - 16]):
+        with pytest.raises(ma.AdamError) as e:
+            ma.adam_state_set_draw_index(st, bad)
+        assert e.value.code == -1, bad
+    assert ma.adam_state_get_draw_index(st) == [0, 5008]
+    ma.adam_state_set_draw_index(st, [2 ** 40, 16])
+    params = workloads.host_params(42, numels)
+    dev_p = [torch.from_numpy(x.copy()).cuda() for x in params]
+    hp = dict(HP, stochastic=True, seed=3)
+    grads = [to_device_grads(workloads.host_grads(42, numels, t), "f32") for t in range(1, 5)]
+    for t in (1, 2):
+        ma.adam_step(st, dev_p, grads[t - 1], t=t, **hp)
+    st2 = ma.adam_state_load(ma.adam_state_save(st))
+    assert ma.adam_state_get_draw_index(st2) == [2 ** 40, 16]
+    p2 = [x.clone() for x in dev_p]
+    for t in (3, 4):
+        ma.adam_step(st, dev_p, grads[t - 1], t=t, **hp)
+        ma.adam_step(st2, p2, grads[t - 1], t=t, **hp)
+    torch.cuda.synchronize()
+    a, b = read_state(st), read_state(st2)
+    for nm in a:
+        assert np.array_equal(a[nm].view(np.uint8), b[nm].view(np.uint8)), nm
+    for x, y in zip(dev_p, p2):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    # the draws did move: the default indices give other codes
+    st3 = ma.adam_state_create(numels, "q8", "f32")
+    p3 = [torch.from_numpy(x.copy()).cuda() for x in params]
+    for t in (1, 2, 3, 4):
+        ma.adam_step(st3, p3, grads[t - 1], t=t, **hp)
+    torch.cuda.synchronize()
+    assert not np.array_equal(read_state(st3)["m_codes"], a["m_codes"])
+    for x in (st, st2, st3):
+        x.destroy()
 
 
 def test_single_tensor_1m_q8_ten_steps():
@@ -572,7 +677,7 @@ def test_checkpoint_resume_is_bit_exact(storage, gdt, sr, pct, ams):
     saved_p = [x.clone() for x in dev_p]
     # the stream's records are the state buffers, verbatim
     got = read_state(st)
-    off = 40 + 8 * len(numels)
+    off = 40 + 16 * len(numels)
     names = {"bf16": ["m_bf16", "v_bf16"], "q8": ["m_codes", "v_codes", "m_scale", "v_scale"],
              "q8_v_only": ["v_codes", "v_scale", "m_f32"]}[storage]
     if ams:
