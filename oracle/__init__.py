@@ -38,13 +38,16 @@ _vp = ctypes.c_void_p
 
 
 def lib():
-    """Load (building first if absent) the oracle's shared library."""
+    """Load (building first if absent) the oracle's shared library.  The
+    environment variable ORACLE_LIBRARY names another build of the same
+    source to load instead (the sanitizer tests use it)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIBRARY):
+    path = os.environ.get("ORACLE_LIBRARY") or _build.LIBRARY
+    if path == _build.LIBRARY and not os.path.exists(path):
         _build.build()
-    L = ctypes.CDLL(_build.LIBRARY)
+    L = ctypes.CDLL(path)
     L.orc_bf16_from_f32_array.argtypes = [_f32p, _u16p, ctypes.c_int64]
     L.orc_f32_from_bf16_array.argtypes = [_u16p, _f32p, ctypes.c_int64]
     L.orc_philox4x32_10.argtypes = [_u32p, _u32p, _u32p]
