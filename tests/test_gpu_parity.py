@@ -353,6 +353,51 @@ def test_draw_index_validation_and_checkpoint():
         x.destroy()
 
 
+_GOLDEN = None
+
+
+def _golden():
+    global _GOLDEN
+    if _GOLDEN is None:
+        import json
+        import os
+        with open(os.path.join(os.path.dirname(__file__), "golden", "step_examples.json")) as f:
+            _GOLDEN = json.load(f)
+    return _GOLDEN
+
+
+def _f32(hexes):
+    return np.array([int(h, 16) for h in hexes], np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("name", ["bf16", "bf16_amsgrad_l2", "q8_rne", "q8_sr", "q8_sr_amsgrad",
+                                  "q8_pct50", "q8_v_only_sr_pct"])
+def test_stored_step_examples(name):
+    # the stored examples (written from the oracle, kept in the repository)
+    G = _golden()
+    case = G["cases"][name]
+    numels = G["numels"]
+    st = ma.adam_state_create(numels, case["storage"], "f32", amsgrad=case["amsgrad"])
+    dev_p = [torch.from_numpy(_f32(p).copy()).cuda() for p in G["params0"]]
+    stats = Stats()
+    for t, want in enumerate(case["steps"], start=1):
+        grads = [_f32(g) for g in G["grads"][t - 1]]
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, stochastic=case["stochastic"],
+                     percentile=case["percentile"], seed=G["seed"], decoupled=case["decoupled"],
+                     **G["hparams"])
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), _f32(want["params"][k]), stats, f"t={t} tensor {k}")
+        got = read_state(st)
+        for nm, ref in want.items():
+            if nm == "params":
+                continue
+            ref = _f32(ref) if got[nm].dtype == np.float32 else np.array(ref, got[nm].dtype)
+            compare_buffer(nm, got[nm], ref, case["stochastic"], stats, f"t={t}")
+    assert stats.params_exact == stats.params
+    st.destroy()
+
+
 def test_single_tensor_1m_q8_ten_steps():
     cfg = workloads.CONFIGS["single_q8"]
     log("single 1M q8 nearest-even, 10 steps")
