@@ -500,7 +500,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
         // moments of the 4-element group
-        float small = __builtin_inff(), big = 0.0f;  // min of |m| and v, max of |m|
+        float m_lo = __builtin_inff(), m_hi = 0.0f, v_lo = __builtin_inff();  // min, max |m|; min v
 #pragma unroll
         for (int i = 4 * j; i < 4 * j + 4; ++i) {
             const float gi = g[i];
@@ -513,22 +513,22 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             mo[i] = m;
             vo[i] = v;
             vmax = fmaxf(vmax, v);
-            big = fmaxf(big, fabsf(m));
-            if constexpr (kAms) small = fminf(small, fminf(fabsf(m), wo[i]));
-            else small = fminf(small, fminf(fabsf(m), v));
+            m_hi = fmaxf(m_hi, fabsf(m));
+            m_lo = fminf(m_lo, fabsf(m));
+            v_lo = fminf(v_lo, kAms ? wo[i] : v);
         }
-        mmax = fmaxf(mmax, big);
+        mmax = fmaxf(mmax, m_hi);
         // p = p*decay - step * m / (sqrt(v) * ibc2 + eps).  When every lane's
-        // group lies in the normal range (|m| and v at least 2^-40, |m| at
-        // most 2^40, so that sqrt(v) * ibc2 + eps is in [2^-40, 2^77] given
-        // ibc2 <= 2^12 and eps in [2^-40, 2^20]) the wave takes the short
-        // sequences, otherwise the general ones.  Same bits either way; one
+        // group lies in the normal range (v at least 2^-96 for sqrt_rn; |m|
+        // in [2^-40, 2^40] for div_rn, whose divisor sqrt(v) * ibc2 + eps is
+        // in [2^-40, 2^77] given ibc2 <= 2^12 and eps in [2^-40, 2^20]) the
+        // wave takes the short sequences, otherwise the general ones.  Same bits either way; one
         // decision per group lets a group's update start while the next
         // group's loads are still in flight.  The percentile variants (whose
         // radix selects dominate) measured faster without the decision and
         // always take the general sequences.
         const float(&vden)[kItems] = kAms ? wo : vo;
-        const bool in_range = a.fast_ok && small >= 0x1p-40f && big <= 0x1p40f;
+        const bool in_range = a.fast_ok && v_lo >= 0x1p-96f && m_lo >= 0x1p-40f && m_hi <= 0x1p40f;
         if (!kPct && __all(in_range)) {
 #pragma unroll
             for (int i = 4 * j; i < 4 * j + 4; ++i) {
