@@ -398,6 +398,36 @@ def test_stored_step_examples(name):
     st.destroy()
 
 
+@pytest.mark.parametrize("storage,gdt,sr,pct,static,ams", [("q8", "bf16", True, None, False, False),
+                                                          ("q8_v_only", "f32", False, 99.9, False, False),
+                                                          ("bf16", "f32", False, None, False, False),
+                                                          ("q8", "f32", True, None, True, True)])
+def test_hundred_steps_stay_bit_exact(storage, gdt, sr, pct, static, ams):
+    # a long run: every element, every 10th step, params bit for bit
+    numels = RAGGED
+    log(f"100 steps {storage} grads={gdt} sr={sr} pct={pct} static={static} amsgrad={ams}")
+    hp = dict(HP, stochastic=sr, percentile=pct, static_scales=static, seed=7)
+    params = workloads.host_params(43, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, storage, gdt, amsgrad=ams)
+    ost = oracle.OracleState(numels, storage, grad_bf16=(gdt == "bf16"), amsgrad=ams)
+    stats = Stats()
+    for t in range(1, 101):
+        grads = workloads.host_grads(43, numels, t, dist="student_t3", dtype=gdt)
+        ma.adam_step(st, dev_p, to_device_grads(grads, gdt), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        if t % 10 == 0:
+            torch.cuda.synchronize()
+            for k in range(len(numels)):
+                compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t} tensor {k}")
+            got = read_state(st)
+            for nm, want in ost.buffers().items():
+                compare_buffer(nm, got[nm], want, sr, stats, f"t={t}")
+    log(f"  {stats}")
+    assert stats.params_exact == stats.params
+    st.destroy()
+
+
 def test_single_tensor_1m_q8_ten_steps():
     cfg = workloads.CONFIGS["single_q8"]
     log("single 1M q8 nearest-even, 10 steps")
