@@ -696,7 +696,18 @@ template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kA
 __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
     __shared__ BlockLds lds;
     __shared__ SelectLds<kPct> sel;
-    for (uint32_t i = blockIdx.x; i < a.n_all; i += gridDim.x) {
+    for (uint32_t i0 = blockIdx.x; i0 < a.n_all; i0 += gridDim.x) {
+        // XCD-aware order: workgroup i0 runs on XCD i0 mod 8, and here each
+        // XCD takes runs of 16 consecutive blocks, the runs dealt round-robin
+        // (a bijection on the first n - n mod 128 blocks; the rest keep their
+        // order).  Measured +2% for the 8-bit nearest-rounding step and ~+1%
+        // for the percentile one; the VALU-bound stochastic-rounding steps
+        // keep plain order (-0.4% with it).
+        uint32_t i = i0;
+        if (!kSR && gridDim.x == a.n_all && i0 < a.n_all - a.n_all % 128u) {
+            const uint32_t x = i0 & 7u, k = i0 >> 3;
+            i = ((k >> 4) << 7) + (x << 4) + (k & 15u);
+        }
         BlockRegs<kStore, kGradBf16, kAms> r;
         const BlockCtx c = load_ctx<kGradBf16>(a, i);
         if (i < a.n_full) {
@@ -706,7 +717,7 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
             load_data<kStore, kGradBf16, kAms, false>(a, c, r);
             process_block<kStore, kGradBf16, kSR, kPct, kStatic, kAms, false>(a, c, r, lds, sel);
         }
-        if (i + gridDim.x < a.n_all) __syncthreads();  // LDS reused by the next block
+        if (i0 + gridDim.x < a.n_all) __syncthreads();  // LDS reused by the next block
     }
 }
 
