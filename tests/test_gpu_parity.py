@@ -659,6 +659,54 @@ def test_two_states_interleaved():
     sb.destroy()
 
 
+def test_states_stepped_from_concurrent_threads_and_streams():
+    # different states are independent: four host threads, each with its own
+    # state, stream and rotating gradient buffers (so the pointer-table cache
+    # and staging ring are exercised), step concurrently without any host
+    # synchronization between them; each result must equal its oracle run
+    import threading
+    specs = [([3000, 17], "q8", "f32", True), ([2049, 5000], "bf16", "bf16", False),
+             ([6001], "q8_v_only", "bf16", True), ([4096, 1, 300], "q8", "bf16", False)]
+    runs, errors = [], []
+    for i, (numels, storage, gdt, sr) in enumerate(specs):
+        params = workloads.host_params(60 + i, numels)
+        grads = [workloads.host_grads(60 + i, numels, t, dtype=gdt) for t in range(1, 13)]
+        runs.append(dict(numels=numels, storage=storage, gdt=gdt, sr=sr, params=params, grads=grads,
+                         dev_p=[torch.from_numpy(x.copy()).cuda() for x in params],
+                         dev_g=[to_device_grads(g, gdt) for g in grads],
+                         stream=torch.cuda.Stream(),
+                         st=ma.adam_state_create(numels, storage, gdt)))
+    torch.cuda.synchronize()
+
+    def work(r):
+        try:
+            for t in range(1, 13):
+                ma.adam_step(r["st"], r["dev_p"], r["dev_g"][t - 1], t=t, stochastic=r["sr"], seed=11,
+                             stream=r["stream"], **HP)
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(r,)) for r in runs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    stats = Stats()
+    for r in runs:
+        o = oracle.OracleState(r["numels"], r["storage"], grad_bf16=(r["gdt"] == "bf16"))
+        for t in range(1, 13):
+            o.step(r["params"], r["grads"][t - 1], t=t, stochastic=r["sr"], seed=11, **HP)
+        for d, h in zip(r["dev_p"], r["params"]):
+            compare_params(d.cpu().numpy(), h, stats)
+        got = read_state(r["st"])
+        for nm, want in o.buffers().items():
+            compare_buffer(nm, got[nm], want, r["sr"], stats)
+        r["st"].destroy()
+    assert stats.params_exact == stats.params
+
+
 def test_error_paths_enqueue_nothing():
     numels = [100]
     st = ma.adam_state_create(numels, "q8")
