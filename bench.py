@@ -120,6 +120,8 @@ def main():
                     help="8-bit sets: keep each block's scale once set")
     ap.add_argument("--amsgrad", action="store_true",
                     help="keep the running maximum of v (AMSGrad)")
+    ap.add_argument("--percentile", type=float, default=None,
+                    help="8-bit sets: percentile block statistic (e.g. 99.9) instead of the set's own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's device copy of 4 GiB (counter calibration run)")
     args = ap.parse_args()
@@ -161,6 +163,10 @@ def main():
         if cfg.storage == "bf16":
             sys.exit("bench.py: --static-scales applies to 8-bit storage only")
         hp["static_scales"] = True
+    if args.percentile is not None:
+        if cfg.storage == "bf16":
+            sys.exit("bench.py: --percentile applies to 8-bit storage only")
+        hp["percentile"] = args.percentile
 
     t = 0
     for _ in range(args.warmup):
@@ -188,9 +194,9 @@ def main():
 
     alg = algorithmic_bytes(cfg)
     achieved = alg / sec / 1e9
-    # counter readings are taken per workload for the dynamic-scale,
-    # plain-Adam kernel
-    traffic = None if (args.static_scales or cfg.amsgrad) else traffic_for(cfg.name)
+    # counter readings are taken per workload for its own kernel variant
+    variant_changed = args.static_scales or cfg.amsgrad or args.percentile is not None
+    traffic = None if variant_changed else traffic_for(cfg.name)
     out = {
         "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",
         "value": round(n_params / sec / 1e9, 3),
