@@ -3,11 +3,12 @@
 // One 256-thread workgroup (4 wave64s) owns one 2048-element block: it
 // reads the block's params, grads, stored moments and old scales once,
 // keeps the updated moments in registers, reduces the block statistic
-// (DPP cross-lane steps + one cross-wave LDS step; an LDS radix select for
-// the percentile statistic; skipped for a moment whose static scale is
-// already set), requantizes and writes params, moments and the new scales
-// once.  With AMSGrad the running maximum of v travels the same way as v.  The step is a streaming map over HBM (14-20 bytes per
-// parameter, ~1.5 flop/byte), so there is no MFMA work; what matters is
+// (DPP cross-lane steps + one cross-wave LDS step; for the percentile
+// statistic, per-wave walks down the top values or an LDS radix select;
+// skipped for a moment whose static scale is already set), requantizes and
+// writes params, moments and the new scales once.  With AMSGrad the running
+// maximum of v travels the same way as v.  The step is a streaming map over
+// HBM (14-20 bytes per parameter, ~1.5 flop/byte), so there is no MFMA work; what matters is
 // coalesced 16-byte loads, enough bytes in flight per CU and a VALU budget
 // of roughly 100 instructions per element at the bandwidth target.
 //
@@ -206,6 +207,90 @@ __device__ uint32_t block_select(const uint32_t (&key)[kItems], uint32_t rank, u
     return prefix;
 }
 
+// The same statistic when it lies near the top: the rank-th smallest of the
+// 2048 keys is the need-th largest, need = 2048 - rank, counted with
+// multiplicity.  A high percentile (99.9 of a full block: need 4) makes
+// need small, and then two walks down the distinct values replace the radix
+// passes (the launch picks one path or the other for the whole step, see
+// walk_covers):
+//   wave_top:  each wave takes its own keys' largest value, counts it,
+//              drops it, and repeats until at least `need` keys are counted;
+//              the (value, count) list goes to LDS.  No barrier.
+//   top_merge: after one barrier, the same walk over the union of the four
+//              lists (64 entries, one per lane), stopping at `need`.
+// The union walk is exact: each wave's list holds every key of that wave
+// down to its last value L_w, with counts, and the answer s has at least
+// `need` keys at or above it in the block, so s >= max_w L_w; at and above
+// that point the union counts every key, and s is in its own wave's list
+// (fewer than `need` keys of the block lie above it).
+// Keys are stored plus one, so 0 marks "dropped" / "empty" and the unsigned
+// max with its identity 0 serves both walks.
+constexpr uint32_t kTopCap = 16;  // largest need taken by the walks
+static_assert(kWaves * kTopCap == 64, "one union entry per lane");
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, dpp<kQuadPerm1032>(x));
+    x = max(x, dpp<kQuadPerm2301>(x));
+    x = max(x, dpp<kRowRor4>(x));
+    x = max(x, dpp<kRowRor8>(x));
+    x = max(x, dpp<kRowBcast15, 0xA>(x));
+    x = max(x, dpp<kRowBcast31, 0xC>(x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// top values of |x| over the wave's 512 keys; writes kTopCap (value+1,
+// count) entries at val[wave * kTopCap ...], unused entries (0, 0).
+// need in [1, kTopCap], wave-uniform.
+__device__ __forceinline__ void wave_top(const float (&x)[kItems], uint32_t need, uint32_t *val,
+                                         uint32_t *cnt) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t key[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) key[i] = (__float_as_uint(x[i]) & 0x7FFFFFFFu) + 1u;
+    uint32_t my_val = 0u, my_cnt = 0u, acc = 0u;
+    // each round counts at least one key (the wave holds 512 > kTopCap), so
+    // kTopCap rounds always reach need
+    for (uint32_t it = 0; it < kTopCap; ++it) {
+        uint32_t lm = key[0];
+#pragma unroll
+        for (int i = 1; i < kItems; ++i) lm = max(lm, key[i]);
+        const uint32_t M = wave_max_u32(lm);
+        uint32_t C = 0u;
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) {
+            const bool hit = key[i] == M;
+            C += (uint32_t)__popcll(__ballot(hit));
+            key[i] = hit ? 0u : key[i];
+        }
+        if (lane == (int)it) { my_val = M; my_cnt = C; }
+        acc += C;
+        if (acc >= need) break;
+    }
+    if (lane < (int)kTopCap) {
+        val[wave * kTopCap + lane] = my_val;
+        cnt[wave * kTopCap + lane] = my_cnt;
+    }
+}
+
+// need-th largest key over the union of the wave lists (after a barrier
+// that follows every wave_top); every wave computes it.
+__device__ __forceinline__ uint32_t top_merge(const uint32_t *val, const uint32_t *cnt, uint32_t need) {
+    const int lane = threadIdx.x & 63;
+    uint32_t v = val[lane];
+    const uint32_t n = cnt[lane];
+    uint32_t acc = 0u, M = 1u;
+    // each round consumes at least one entry of count >= 1, and the entries
+    // hold at least need counts in total, so the walk stops within 64 rounds
+    for (int it = 0; it < 64; ++it) {
+        M = wave_max_u32(v);
+        const uint32_t s = wave_inclusive_sum(v == M ? n : 0u);
+        acc += (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
+        if (acc >= need) break;
+        v = v == M ? 0u : v;
+    }
+    return M - 1u;
+}
+
 // ---------------------------------------------------------------- quantizer
 // Code magnitude for |x| = a with statistic A and r = fl(qmax/A) (A >= kTiny).
 // For a < A, a <= A(1 - 2^-24) and r <= (qmax/A)(1 + 2^-24), so y = fl(a*r) <=
@@ -382,18 +467,22 @@ struct BlockLds {
     float red[3][kWaves];
 };
 
-// LDS of the percentile statistic (radix-select histogram + scan scratch).
-template <bool kPct>
-struct SelectLds {
-    __device__ uint32_t *hist() { return nullptr; }
-    __device__ uint32_t *scratch() { return nullptr; }
+// Block statistic of a step: the block maximum, or the percentile taken by
+// the top walks or by the radix select.
+enum PctMode { kPctNone = 0, kPctTop = 1, kPctRadix = 2 };
+
+// LDS of the percentile statistic.
+template <int kPct>
+struct SelectLds {};
+template <>
+struct SelectLds<kPctTop> {  // wave lists of the walks (m, v, AMSGrad maximum)
+    uint32_t val[3][kWaves * kTopCap];
+    uint32_t cnt[3][kWaves * kTopCap];
 };
 template <>
-struct SelectLds<true> {
+struct SelectLds<kPctRadix> {  // histogram + scan scratch
     uint32_t h[kBlock];
     uint32_t s[kWaves + 2];
-    __device__ uint32_t *hist() { return h; }
-    __device__ uint32_t *scratch() { return s; }
 };
 
 // ---------------------------------------------------------------- exact sqrt / divide
@@ -459,7 +548,7 @@ __device__ __forceinline__ float uniform(float x) {
 // skips its statistic; values at or beyond it saturate through the end rule.
 // kAms: AMSGrad -- the running maximum w of v is decoded, updated to
 // max(w, v), used in the denominator and stored as v is, with its own scale.
-template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kAms, bool kFull>
+template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAms, bool kFull>
 __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx &c,
                                               const BlockRegs<kStore, kGradBf16, kAms> &r,
                                               BlockLds &lds, SelectLds<kPct> &sel) {
@@ -529,7 +618,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         // always take the general sequences.
         const float(&vden)[kItems] = kAms ? wo : vo;
         const bool in_range = a.fast_ok && v_lo >= 0x1p-96f && m_lo >= 0x1p-40f && m_hi <= 0x1p40f;
-        if (!kPct && __all(in_range)) {
+        if (__all(in_range)) {
 #pragma unroll
             for (int i = 4 * j; i < 4 * j + 4; ++i) {
                 const float den = fmaf(sqrt_rn(vden[i]), a.ibc2, a.eps);
@@ -594,6 +683,20 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             }
         }
         const bool need_m = kQuantM && !keep_m, need_v = !keep_v, need_w = kAms && !keep_w;
+        // percentile: rank-th smallest of the block's 2048 keys (the padding
+        // adds zeros below the n values), i.e. the need-th largest
+        uint32_t rank = 0, need = 0;
+        if constexpr (kPct != kPctNone) {
+            rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
+            need = kBlock - rank;  // in [1, kTopCap] for kPctTop (walk_covers)
+        }
+        if constexpr (kPct == kPctTop) {  // wave walks; the barrier in block_max publishes their lists
+            if (need_m) wave_top(mo, need, sel.val[0], sel.cnt[0]);
+            if (need_v) wave_top(vo, need, sel.val[1], sel.cnt[1]);
+            if constexpr (kAms)
+                if (need_w) wave_top(wo, need, sel.val[2], sel.cnt[2]);
+        }
+        static_assert(kWaves > 1, "block_max's barrier orders the wave lists");
         if (need_m || need_v || need_w) {
             if constexpr (kAms) {
                 float x[3] = {mmax, vmax, wmax};
@@ -606,31 +709,33 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             }
         }
         float Amn = keep_m ? Am_old : mmax, Avn = keep_v ? Av_old : vmax, Awn = keep_w ? Aw_old : wmax;
-        if constexpr (kPct) {
-            const uint32_t rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
-            uint32_t key[kItems];
-            if (need_m) {
+        if constexpr (kPct != kPctNone) {
+            auto stat = [&](const float (&x)[kItems], int which) -> float {
+                if constexpr (kPct == kPctTop) {
+                    return __uint_as_float(top_merge(sel.val[which], sel.cnt[which], need));
+                } else {
+                    uint32_t key[kItems];
 #pragma unroll
-                for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(mo[i]) & 0x7FFFFFFFu;
-                const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
+                    for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(x[i]) & 0x7FFFFFFFu;
+                    return __uint_as_float(block_select(key, rank, sel.h, sel.s));
+                }
+            };
+            if (need_m) {
+                const float sv = stat(mo, 0);
                 Amn = sv < kTiny ? mmax : sv;
             }
             if (need_v) {
-#pragma unroll
-                for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(vo[i]) & 0x7FFFFFFFu;
-                const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
+                const float sv = stat(vo, 1);
                 Avn = sv < kTiny ? vmax : sv;
             }
             if constexpr (kAms) {
                 if (need_w) {
-#pragma unroll
-                    for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(wo[i]) & 0x7FFFFFFFu;
-                    const float sv = __uint_as_float(block_select(key, rank, sel.hist(), sel.scratch()));
+                    const float sv = stat(wo, 2);
                     Awn = sv < kTiny ? wmax : sv;
                 }
             }
         }
-        constexpr bool kPin = kSR || kPct || kStatic;
+        constexpr bool kPin = kSR || kPct != kPctNone || kStatic;
         const bool mzero = !(Amn >= kTiny), vzero = !(Avn >= kTiny), wzero = !(Awn >= kTiny);
         const float rm = mzero ? 0.0f : 127.0f / Amn;
         const float rv = vzero ? 0.0f : 255.0f / Avn;
@@ -692,7 +797,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 // One workgroup per block; workgroups beyond the grid limit loop (stride =
 // grid size).  Descriptors [0, n_full) are full blocks, whose path has no
 // tail checks; the rest are the tensors' ragged last blocks.
-template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kAms>
+template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAms>
 __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
     __shared__ BlockLds lds;
     __shared__ SelectLds<kPct> sel;
@@ -737,7 +842,7 @@ constexpr int kCuLdsBytes = 160 * 1024;
 constexpr size_t reserve_lds(int resident) { return resident >= 8 ? 0 : kCuLdsBytes / (resident + 1) + 1024; }
 constexpr uint32_t kMaxGrid = (1u << 24) - 1;  // grid.x * 256 work-items < 2^32
 
-template <int kStore, bool kGradBf16, bool kSR, bool kPct, bool kStatic, bool kAms>
+template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAms>
 hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     const uint32_t grid = std::min<uint32_t>(a.n_all, kMaxGrid);
     if (grid == 0) return hipSuccess;
@@ -749,13 +854,25 @@ hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The walks serve a step when every block's need is at most kTopCap.  need =
+// n - floor(p (n - 1)) for a block of n values never falls as n grows (n + 1
+// raises the floor by 0 or 1), so the full block's need decides; the double
+// arithmetic is the kernel's own, so both sides agree on it.
+bool walk_covers(double pfrac) {
+    return (uint32_t)kBlock - (uint32_t)floor(pfrac * (double)(kBlock - 1)) <= kTopCap;
+}
+
+template <int kStore, bool kGradBf16, bool kSR, bool kStatic, bool kAms>
+hipError_t launch_stat(const Variant &v, const StepArgs &a, hipStream_t stream) {
+    if (!v.percentile) return launch_one<kStore, kGradBf16, kSR, kPctNone, kStatic, kAms>(a, stream);
+    return walk_covers(a.pfrac) ? launch_one<kStore, kGradBf16, kSR, kPctTop, kStatic, kAms>(a, stream)
+                                : launch_one<kStore, kGradBf16, kSR, kPctRadix, kStatic, kAms>(a, stream);
+}
+
 template <int kStore, bool kGradBf16, bool kStatic, bool kAms>
 hipError_t launch_rounding(const Variant &v, const StepArgs &a, hipStream_t stream) {
-    if (v.stochastic)
-        return v.percentile ? launch_one<kStore, kGradBf16, true, true, kStatic, kAms>(a, stream)
-                            : launch_one<kStore, kGradBf16, true, false, kStatic, kAms>(a, stream);
-    return v.percentile ? launch_one<kStore, kGradBf16, false, true, kStatic, kAms>(a, stream)
-                        : launch_one<kStore, kGradBf16, false, false, kStatic, kAms>(a, stream);
+    return v.stochastic ? launch_stat<kStore, kGradBf16, true, kStatic, kAms>(v, a, stream)
+                        : launch_stat<kStore, kGradBf16, false, kStatic, kAms>(v, a, stream);
 }
 
 template <int kStore, bool kGradBf16, bool kAms>
@@ -768,8 +885,8 @@ template <bool kAms>
 hipError_t launch_storage(const Variant &v, const StepArgs &a, hipStream_t stream) {
     switch (v.storage) {
     case kStoreBf16:
-        return v.grad_bf16 ? launch_one<kStoreBf16, true, false, false, false, kAms>(a, stream)
-                           : launch_one<kStoreBf16, false, false, false, false, kAms>(a, stream);
+        return v.grad_bf16 ? launch_one<kStoreBf16, true, false, kPctNone, false, kAms>(a, stream)
+                           : launch_one<kStoreBf16, false, false, kPctNone, false, kAms>(a, stream);
     case kStoreQ8:
         return v.grad_bf16 ? launch_q<kStoreQ8, true, kAms>(v, a, stream)
                            : launch_q<kStoreQ8, false, kAms>(v, a, stream);

@@ -133,6 +133,29 @@ def test_static_scales_set_late_and_mixed_with_dynamic_steps(storage):
     st.destroy()
 
 
+# percentiles whose full-block rank lands near the top: need = 2048 - rank
+# keys at or above the statistic, with rank = floor(p/100 * 2047).  Up to
+# 16 the kernel walks down the top values per wave, beyond it it takes the
+# radix select; 2032.5 and 2031.5 sit on either side of that switch.
+NEAR_TOP = [100.0, 99.9, 99.5, 100.0 * 2032.5 / 2047, 100.0 * 2031.5 / 2047]
+
+
+@pytest.mark.parametrize("pct", NEAR_TOP)
+@pytest.mark.parametrize("storage,gdt,sr,ams", [("q8", "f32", False, False),
+                                                ("q8", "bf16", True, True),
+                                                ("q8_v_only", "f32", False, True)])
+def test_percentile_near_the_top_with_ties(pct, storage, gdt, sr, ams):
+    # gradients of five values tie the moments of a block in large groups,
+    # so the top values come with counts far above need; the outlier set
+    # puts a few isolated large values above the rest
+    log(f"percentile {pct:.6f} {storage} grads={gdt} sr={sr} amsgrad={ams}")
+    hp = dict(HP, beta2=0.9, stochastic=sr, percentile=pct, seed=5)
+    for dist in ("few_levels", "normal_outliers"):
+        stats = run_full_parity(RAGGED, storage, gdt, 4, hp, cfg_id=15, grad_dist=dist,
+                                amsgrad=ams)
+        log(f"  {dist}: {stats}")
+
+
 AMSGRAD_MODES = [
     # storage, grad dtype, stochastic, percentile, static scales, decoupled, beta2
     ("bf16", "f32", False, None, False, True, 0.9),

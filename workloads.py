@@ -135,7 +135,7 @@ class Config:
     shapes_fn: object
     storage: str            # "bf16" | "q8" | "q8_v_only"
     grad_dtype: str         # "f32" | "bf16"
-    grad_dist: str          # "normal" | "student_t3" | "normal_outliers"
+    grad_dist: str          # "normal" | "student_t3" | "normal_outliers" (| "few_levels", host only)
     steps: int
     hp: dict = field(default_factory=dict)
     amsgrad: bool = False   # the state keeps the running maximum of v
@@ -200,6 +200,9 @@ def host_grads(cfg_id, numels, t, dist="normal", dtype="f32"):
             g = rng.standard_normal(n, dtype=np.float32) * np.float32(1e-3)
             hit = rng.random(n) < 1e-3
             g[hit] *= np.float32(100.0)
+        elif dist == "few_levels":
+            # five gradient values: the moments of a block tie in large groups
+            g = (rng.integers(-2, 3, size=n) * 1e-3).astype(np.float32)
         else:
             raise ValueError(dist)
         out.append(bf16_bits_of(g) if dtype == "bf16" else g)
