@@ -217,7 +217,9 @@ __device__ uint32_t block_select(const uint32_t (&key)[kItems], uint32_t rank, u
 //              drops it, and repeats until at least `need` keys are counted;
 //              the (value, count) list goes to LDS.  No barrier.
 //   top_merge: after one barrier, the same walk over the union of the four
-//              lists (64 entries, one per lane), stopping at `need`.
+//              lists (64 entries, one per lane), stopping at `need`; wave k
+//              merges moment k and publishes it through LDS (one more
+//              barrier), so the merges cost one wave each.
 // The union walk is exact: each wave's list holds every key of that wave
 // down to its last value L_w, with counts, and the answer s has at least
 // `need` keys at or above it in the block, so s >= max_w L_w; at and above
@@ -238,6 +240,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
+__device__ __forceinline__ uint32_t top_key(float x) { return (__float_as_uint(x) & 0x7FFFFFFFu) + 1u; }
+
 // top values of |x| over the wave's 512 keys; writes kTopCap (value+1,
 // count) entries at val[wave * kTopCap ...], unused entries (0, 0).
 // need in [1, kTopCap], wave-uniform.
@@ -246,7 +250,7 @@ __device__ __forceinline__ void wave_top(const float (&x)[kItems], uint32_t need
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t key[kItems];
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) key[i] = (__float_as_uint(x[i]) & 0x7FFFFFFFu) + 1u;
+    for (int i = 0; i < kItems; ++i) key[i] = top_key(x[i]);
     uint32_t my_val = 0u, my_cnt = 0u, acc = 0u;
     // each round counts at least one key (the wave holds 512 > kTopCap), so
     // kTopCap rounds always reach need
@@ -272,21 +276,83 @@ __device__ __forceinline__ void wave_top(const float (&x)[kItems], uint32_t need
     }
 }
 
+// The same walk for need <= kPairNeed with less work per round: each lane
+// first keeps only its two largest keys (a >= b), and the rounds look at
+// those.  While every lane still holds a known key, the largest of them is
+// the wave's largest remaining key.  A lane whose known keys are both taken
+// (by two rounds, or by one value tied in the lane) may hide more keys at or
+// above the next value: if need is not reached by then, the wave returns
+// false and takes the full walk.  The round that reaches need may miss such
+// tied keys in its count; the merge stays exact, since that count is still
+// at least need, and only the counts above the last value enter its sums
+// below the answer.  For need <= 4 a wave falls back only when one lane
+// holds two of its three largest keys (~4% of waves for distinct keys).
+constexpr uint32_t kPairNeed = 4;
+
+__device__ __forceinline__ bool wave_top_pairs(const float (&x)[kItems], uint32_t need, uint32_t *val,
+                                               uint32_t *cnt) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t a = top_key(x[0]), b = top_key(x[1]);
+    {
+        const uint32_t hi = max(a, b);
+        b = min(a, b);
+        a = hi;
+    }
+#pragma unroll
+    for (int i = 2; i < kItems; ++i) {
+        const uint32_t k = top_key(x[i]);
+        b = max(b, min(a, k));
+        a = max(a, k);
+    }
+    uint32_t my_val = 0u, my_cnt = 0u, acc = 0u;
+    for (uint32_t it = 0; it < kPairNeed; ++it) {
+        const uint32_t M = wave_max_u32(a);
+        const bool ha = a == M, hb = b == M;  // hb implies ha
+        const uint32_t C = (uint32_t)__popcll(__ballot(ha)) + (uint32_t)__popcll(__ballot(hb));
+        if (lane == (int)it) { my_val = M; my_cnt = C; }
+        acc += C;
+        if (acc >= need) break;
+        if (__ballot(ha && (hb || b == 0u)) != 0) return false;  // a lane without a known key
+        a = ha ? b : a;
+        b = ha ? 0u : b;
+    }
+    if (lane < (int)kTopCap) {
+        val[wave * kTopCap + lane] = my_val;
+        cnt[wave * kTopCap + lane] = my_cnt;
+    }
+    return true;
+}
+
+__device__ __forceinline__ void wave_top_any(const float (&x)[kItems], uint32_t need, uint32_t *val,
+                                             uint32_t *cnt) {
+    if (need > kPairNeed || !wave_top_pairs(x, need, val, cnt)) wave_top(x, need, val, cnt);
+}
+
 // need-th largest key over the union of the wave lists (after a barrier
-// that follows every wave_top); every wave computes it.
+// that follows every wave_top), computed by one wave.  Each round
+// consumes at least one entry of count >= 1, and the entries hold at least
+// need counts in total, so the walk stops within 64 rounds.
 __device__ __forceinline__ uint32_t top_merge(const uint32_t *val, const uint32_t *cnt, uint32_t need) {
     const int lane = threadIdx.x & 63;
     uint32_t v = val[lane];
     const uint32_t n = cnt[lane];
     uint32_t acc = 0u, M = 1u;
-    // each round consumes at least one entry of count >= 1, and the entries
-    // hold at least need counts in total, so the walk stops within 64 rounds
-    for (int it = 0; it < 64; ++it) {
-        M = wave_max_u32(v);
-        const uint32_t s = wave_inclusive_sum(v == M ? n : 0u);
-        acc += (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
-        if (acc >= need) break;
-        v = v == M ? 0u : v;
+    if (__ballot(n > 1u) == 0) {  // every entry one key (distinct values): a ballot counts a round
+        for (int it = 0; it < 64; ++it) {
+            M = wave_max_u32(v);
+            const bool hit = v == M;
+            acc += (uint32_t)__popcll(__ballot(hit));
+            if (acc >= need) break;
+            v = hit ? 0u : v;
+        }
+    } else {
+        for (int it = 0; it < 64; ++it) {
+            M = wave_max_u32(v);
+            const uint32_t s = wave_inclusive_sum(v == M ? n : 0u);
+            acc += (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
+            if (acc >= need) break;
+            v = v == M ? 0u : v;
+        }
     }
     return M - 1u;
 }
@@ -478,6 +544,7 @@ template <>
 struct SelectLds<kPctTop> {  // wave lists of the walks (m, v, AMSGrad maximum)
     uint32_t val[3][kWaves * kTopCap];
     uint32_t cnt[3][kWaves * kTopCap];
+    uint32_t res[3];  // merged statistic of each moment
 };
 template <>
 struct SelectLds<kPctRadix> {  // histogram + scan scratch
@@ -691,10 +758,10 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             need = kBlock - rank;  // in [1, kTopCap] for kPctTop (walk_covers)
         }
         if constexpr (kPct == kPctTop) {  // wave walks; the barrier in block_max publishes their lists
-            if (need_m) wave_top(mo, need, sel.val[0], sel.cnt[0]);
-            if (need_v) wave_top(vo, need, sel.val[1], sel.cnt[1]);
+            if (need_m) wave_top_any(mo, need, sel.val[0], sel.cnt[0]);
+            if (need_v) wave_top_any(vo, need, sel.val[1], sel.cnt[1]);
             if constexpr (kAms)
-                if (need_w) wave_top(wo, need, sel.val[2], sel.cnt[2]);
+                if (need_w) wave_top_any(wo, need, sel.val[2], sel.cnt[2]);
         }
         static_assert(kWaves > 1, "block_max's barrier orders the wave lists");
         if (need_m || need_v || need_w) {
@@ -709,10 +776,23 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             }
         }
         float Amn = keep_m ? Am_old : mmax, Avn = keep_v ? Av_old : vmax, Awn = keep_w ? Aw_old : wmax;
+        if constexpr (kPct == kPctTop) {
+            // wave k merges moment k's lists and publishes the statistic
+            const int wave = threadIdx.x >> 6;
+            const bool need_k[3] = {need_m, need_v, need_w};
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                if (wave == k && need_k[k]) {
+                    const uint32_t st = top_merge(sel.val[k], sel.cnt[k], need);
+                    if ((threadIdx.x & 63) == 0) sel.res[k] = st;
+                }
+            }
+            __syncthreads();
+        }
         if constexpr (kPct != kPctNone) {
             auto stat = [&](const float (&x)[kItems], int which) -> float {
                 if constexpr (kPct == kPctTop) {
-                    return __uint_as_float(top_merge(sel.val[which], sel.cnt[which], need));
+                    return __uint_as_float(sel.res[which]);
                 } else {
                     uint32_t key[kItems];
 #pragma unroll
