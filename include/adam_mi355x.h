@@ -183,8 +183,11 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
  * Errors (no work enqueued): EINVAL (NULL state/params/grads/hp/expect,
  * hyperparameter outside its domain, unknown flag bits, reserved != 0,
  * STOCHASTIC, PERCENTILE or STATIC_SCALES with BF16 storage, call from a
- * device other than the one the state was created on), EMODE, EALIGN;
- * EDEVICE if the launch fails.  Device faults surface on the caller's next synchronization.
+ * device other than the one the state was created on, hip_stream in HIP
+ * graph capture: a captured launch would replay this call's t and
+ * hyperparameters with a pointer table that later calls may re-use), EMODE,
+ * EALIGN; EDEVICE if the launch fails.  Device faults surface on the
+ * caller's next synchronization.
  */
 int adam_step(adam_state *s, float *const *params, const void *const *grads,
               const adam_hparams *hp, const adam_layout *expect, void *hip_stream);

@@ -675,6 +675,14 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
             return fail(ADAM_EINVAL, "state lives on device " + std::to_string(s->device) + ", current is " +
                                          std::to_string(dev));
         hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+        // A graph would replay this call's t and hyperparameters, and the
+        // pointer table it names may be re-used by later calls (and a new
+        // one's upload would read a recycled host staging slot at replay):
+        // refuse before recording anything.
+        hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+        if ((e = hipStreamIsCapturing(stream, &capture)) != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (capture != hipStreamCaptureStatusNone)
+            return fail(ADAM_EINVAL, "adam_step cannot be recorded into a graph: the stream is capturing");
 
         // the device pointer table holding these pointers (uploading it if new)
         int slot = -1;

@@ -800,6 +800,61 @@ def test_alternating_gradient_buffers_beyond_the_table_cache():
     st.destroy()
 
 
+def test_step_refuses_a_capturing_stream():
+    # a captured launch would replay one call's t with a pointer table later
+    # calls may re-use: the step is refused while the stream captures, it
+    # records nothing (the capture stays valid and replays its own work),
+    # and eager steps go on as before
+    log("graph capture refused")
+    numels = [4100, 17]
+    params = workloads.host_params(61, numels)
+    dev_p = [torch.from_numpy(x.copy()).cuda() for x in params]
+    grads = [workloads.host_grads(61, numels, t) for t in (1, 2)]
+    dev_g = [[torch.from_numpy(x.copy()).cuda() for x in gs] for gs in grads]
+    st = ma.adam_state_create(numels, "q8")
+    ost = oracle.OracleState(numels, "q8")
+    ma.adam_step(st, dev_p, dev_g[0], t=1, **HP)  # eager: the pointer table is resident
+    ost.step(params, grads[0], t=1, **HP)
+    torch.cuda.synchronize()
+    before_p = [x.clone() for x in dev_p]
+    before_s = read_state(st)
+    x = torch.zeros(64, device="cuda")
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        try:
+            x.add_(1.0)
+            with pytest.raises(ma.AdamError) as e:
+                ma.adam_step(st, dev_p, dev_g[1], t=2, stream=side, **HP)
+            assert e.value.code == -1
+            assert "graph" in ma.adam_last_error()
+        finally:
+            graph.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(x, torch.full_like(x, 3.0))
+    for a, b in zip(dev_p, before_p):
+        assert torch.equal(a, b)
+    after_s = read_state(st)
+    for nm, want in before_s.items():
+        assert np.array_equal(after_s[nm], want), nm
+    ma.adam_step(st, dev_p, dev_g[1], t=2, **HP)
+    ost.step(params, grads[1], t=2, **HP)
+    torch.cuda.synchronize()
+    stats = Stats()
+    for k in range(len(numels)):
+        compare_params(dev_p[k].cpu().numpy(), params[k], stats, "t=2")
+    got = read_state(st)
+    for nm, want in ost.buffers().items():
+        compare_buffer(nm, got[nm], want, False, stats, "t=2")
+    del graph
+    st.destroy()
+
+
 @pytest.mark.parametrize("storage,gdt,sr,pct,ams", [("bf16", "f32", False, None, False),
                                                     ("q8", "bf16", True, None, False),
                                                     ("q8_v_only", "bf16", False, 99.9, False),
