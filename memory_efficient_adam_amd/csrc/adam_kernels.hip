@@ -276,45 +276,86 @@ __device__ __forceinline__ void wave_top(const float (&x)[kItems], uint32_t need
     }
 }
 
-// The same walk for need <= kPairNeed with less work per round: each lane
-// first keeps only its two largest keys (a >= b), and the rounds look at
-// those.  While every lane still holds a known key, the largest of them is
-// the wave's largest remaining key.  A lane whose known keys are both taken
-// (by two rounds, or by one value tied in the lane) may hide more keys at or
-// above the next value: if need is not reached by then, the wave returns
-// false and takes the full walk.  The round that reaches need may miss such
-// tied keys in its count; the merge stays exact, since that count is still
-// at least need, and only the counts above the last value enter its sums
-// below the answer.  For need <= 4 a wave falls back only when one lane
-// holds two of its three largest keys (~4% of waves for distinct keys).
+// The same walk with less work per round: each lane first keeps only its T
+// largest keys, sorted (k[0] >= ... >= k[T-1]), and a round looks at the
+// lanes' heads k[0] only: M = the largest head, counted over the heads
+// equal to it, and those lanes shift their lists up by one.  While every
+// lane still holds a known key, M is the wave's largest remaining key; a
+// value repeated within a lane comes back as M in the next rounds, so it
+// may appear in the list more than once (the merge sums such entries).
+// A lane whose list runs empty may hide more keys at or above the next
+// value: if need is not reached by then, the wave returns false and takes
+// the full walk.  The round that reaches need may miss such hidden copies
+// of M in its count; the merge stays exact, since that count is still at
+// least need, and only the counts above the last value enter its sums
+// below the answer.  T = 2 serves need <= 4 (a wave falls back when one
+// lane holds two of its three largest keys: ~4% of waves for distinct
+// keys), T = 4 serves need <= kTopCap (one lane holding 4 of the wave's 15
+// largest keys: ~0.5% of waves).
 constexpr uint32_t kPairNeed = 4;
 
-__device__ __forceinline__ bool wave_top_pairs(const float (&x)[kItems], uint32_t need, uint32_t *val,
-                                               uint32_t *cnt) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t a = top_key(x[0]), b = top_key(x[1]);
-    {
+// The lane's T largest keys, largest first, in k0..k3 (k2 = k3 = 0 for T =
+// 2).  Named registers rather than an array: the compiler turned the shift
+// of an array into an index-compare chain five times as long.
+template <int T>
+__device__ __forceinline__ void lane_top(const float (&x)[kItems], uint32_t &k0, uint32_t &k1, uint32_t &k2,
+                                         uint32_t &k3) {
+    if constexpr (T == 2) {
+        uint32_t a = top_key(x[0]), b = top_key(x[1]);
         const uint32_t hi = max(a, b);
         b = min(a, b);
         a = hi;
-    }
 #pragma unroll
-    for (int i = 2; i < kItems; ++i) {
-        const uint32_t k = top_key(x[i]);
-        b = max(b, min(a, k));
-        a = max(a, k);
+        for (int i = 2; i < kItems; ++i) {
+            const uint32_t y = top_key(x[i]);
+            b = max(b, min(a, y));
+            a = max(a, y);
+        }
+        k0 = a;
+        k1 = b;
+        k2 = 0u;
+        k3 = 0u;
+    } else {
+        static_assert(T == 4 && kItems == 8, "top 4 of 8 keys");
+        // sort each half with a 5-exchange network, keep the top 4 of the
+        // two (a bitonic sequence), sort it with 4 exchanges
+        auto cx = [](uint32_t &p, uint32_t &q) {  // p >= q afterwards
+            const uint32_t hi = max(p, q);
+            q = min(p, q);
+            p = hi;
+        };
+        uint32_t a0 = top_key(x[0]), a1 = top_key(x[1]), a2 = top_key(x[2]), a3 = top_key(x[3]);
+        uint32_t b0 = top_key(x[4]), b1 = top_key(x[5]), b2 = top_key(x[6]), b3 = top_key(x[7]);
+        cx(a0, a1); cx(a2, a3); cx(a0, a2); cx(a1, a3); cx(a1, a2);
+        cx(b0, b1); cx(b2, b3); cx(b0, b2); cx(b1, b3); cx(b1, b2);
+        k0 = max(a0, b3);
+        k1 = max(a1, b2);
+        k2 = max(a2, b1);
+        k3 = max(a3, b0);
+        cx(k0, k2); cx(k1, k3); cx(k0, k1); cx(k2, k3);
     }
+}
+
+template <int T>
+__device__ __forceinline__ bool wave_top_lanes(const float (&x)[kItems], uint32_t need, uint32_t *val,
+                                               uint32_t *cnt) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t k0, k1, k2, k3;
+    lane_top<T>(x, k0, k1, k2, k3);
     uint32_t my_val = 0u, my_cnt = 0u, acc = 0u;
-    for (uint32_t it = 0; it < kPairNeed; ++it) {
-        const uint32_t M = wave_max_u32(a);
-        const bool ha = a == M, hb = b == M;  // hb implies ha
-        const uint32_t C = (uint32_t)__popcll(__ballot(ha)) + (uint32_t)__popcll(__ballot(hb));
+    // each round counts at least one key, so kTopCap rounds always reach need
+    for (uint32_t it = 0; it < kTopCap; ++it) {
+        const uint32_t M = wave_max_u32(k0);
+        const bool hit = k0 == M;
+        const uint32_t C = (uint32_t)__popcll(__ballot(hit));
         if (lane == (int)it) { my_val = M; my_cnt = C; }
         acc += C;
         if (acc >= need) break;
-        if (__ballot(ha && (hb || b == 0u)) != 0) return false;  // a lane without a known key
-        a = ha ? b : a;
-        b = ha ? 0u : b;
+        k0 = hit ? k1 : k0;
+        k1 = hit ? k2 : k1;
+        k2 = hit ? k3 : k2;
+        k3 = hit ? 0u : k3;
+        if (__ballot(k0 == 0u) != 0) return false;  // a lane without a known key
     }
     if (lane < (int)kTopCap) {
         val[wave * kTopCap + lane] = my_val;
@@ -325,7 +366,9 @@ __device__ __forceinline__ bool wave_top_pairs(const float (&x)[kItems], uint32_
 
 __device__ __forceinline__ void wave_top_any(const float (&x)[kItems], uint32_t need, uint32_t *val,
                                              uint32_t *cnt) {
-    if (need > kPairNeed || !wave_top_pairs(x, need, val, cnt)) wave_top(x, need, val, cnt);
+    const bool done = need <= kPairNeed ? wave_top_lanes<2>(x, need, val, cnt)
+                                        : wave_top_lanes<4>(x, need, val, cnt);
+    if (!done) wave_top(x, need, val, cnt);
 }
 
 // need-th largest key over the union of the wave lists (after a barrier
