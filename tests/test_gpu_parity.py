@@ -156,6 +156,49 @@ def test_percentile_near_the_top_with_ties(pct, storage, gdt, sr, ams):
         log(f"  {dist}: {stats}")
 
 
+def _one_lane_top_grads(seed, numels, t):
+    # in every full block one lane of one wave (lane 5 of wave b mod 4: block
+    # elements 256w + 20 .. + 23 and 1024 + 256w + 20 .. + 23) holds the eight
+    # largest gradients of its wave, distinct and alternating in sign
+    gs = workloads.host_grads(seed, numels, t)
+    for g in gs:
+        for b in range(g.size // 2048):
+            w, lane = b % 4, 5
+            idx = [2048 * b + 256 * w + 4 * lane + k for k in range(4)]
+            idx += [2048 * b + 1024 + 256 * w + 4 * lane + k for k in range(4)]
+            for j, e in enumerate(idx):
+                g[e] = np.float32((-1) ** j * 1e-2 * (1.0 + 0.1 * j + 0.01 * t))
+    return gs
+
+
+@pytest.mark.parametrize("pct", [100.0, 99.9, 99.8, 99.5, 100.0 * 2032.5 / 2047])
+@pytest.mark.parametrize("storage,ams", [("q8", False), ("q8_v_only", True)])
+def test_percentile_walk_lane_lists_run_empty(pct, storage, ams):
+    # the lane holding its wave's largest values empties its short list
+    # (two or four keys) before need is reached in that wave, which then
+    # redoes the full walk; statistic and codes must not change
+    log(f"percentile {pct:.4f} one-lane tops {storage} amsgrad={ams}")
+    numels = [2048 * 4, 3000]
+    hp = dict(HP, beta2=0.9, percentile=pct)
+    params = workloads.host_params(62, numels)
+    dev_p = [torch.from_numpy(x.copy()).cuda() for x in params]
+    st = ma.adam_state_create(numels, storage, amsgrad=ams)
+    ost = oracle.OracleState(numels, storage, amsgrad=ams)
+    stats = Stats()
+    for t in range(1, 5):
+        grads = _one_lane_top_grads(62, numels, t)
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, False, stats, f"t={t}")
+    log(f"  {stats}")
+    st.destroy()
+
+
 AMSGRAD_MODES = [
     # storage, grad dtype, stochastic, percentile, static scales, decoupled, beta2
     ("bf16", "f32", False, None, False, True, 0.9),
