@@ -16,9 +16,14 @@ gets and compares element by element (criteria in tests/parity.py):
   * AMSGrad (running maximum of v) in every storage mode on the ragged set,
     on the full-size GPT-1.3B set with stochastic rounding, and through a
     checkpoint;
+  * the percentile statistic's two paths (top walks, radix select): tied
+    moments, outliers, a wave's largest values in one lane (short lane
+    lists run empty), and percentiles either side of the switch;
+  * seeded random configurations (mode, flags, percentile, hyperparameters,
+    start step, ragged lists, gradient law);
   * edge cases: empty lists and zero-size tensors, a 2^32-1 element tensor,
     injected non-zero states, degenerate hyperparameters, pointer changes,
-    a side stream, and the error paths.
+    a side stream, a refused step under graph capture, and the error paths.
 """
 import ctypes
 import dataclasses
@@ -279,19 +284,19 @@ def _random_case(i):
         numels=[int(x) for x in rng.choice([0, 1, 15, 16, 17, 2047, 2048, 2049, 4100, 6144, 9001],
                                            size=int(rng.integers(1, 5)))],
         t0=int(rng.choice([1, 2, 1000, 100000])),
-        dist=["normal", "student_t3"][int(rng.integers(2))],
+        dist=["normal", "student_t3", "normal_outliers", "few_levels"][int(rng.integers(4))],
         hp=dict(lr=float(rng.choice([1e-4, 1e-3, 1e-1])), beta1=float(rng.choice([0.0, 0.5, 0.9, 0.99])),
                 beta2=float(rng.choice([0.9, 0.99, 0.999, 0.9999])),
                 eps=float(rng.choice([1e-8, 1e-6, 1e-12, 1e-3])),
                 weight_decay=float(rng.choice([0.0, 0.01, 0.1])), decoupled=bool(rng.integers(2)),
                 stochastic=q8 and bool(rng.integers(2)),
-                percentile=(float(rng.choice([0.0, 50.0, 99.0, 99.9, 100.0]))
+                percentile=(float(rng.choice([0.0, 50.0, 99.0, 99.3, 99.5, 99.8, 99.9, 100.0]))
                             if q8 and rng.integers(2) else None),
                 static_scales=q8 and bool(rng.integers(3) == 0), seed=int(rng.integers(2 ** 63))))
     return case
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(36))
 def test_random_configurations(i):
     c = _random_case(i)
     numels, hp, gdt = c["numels"], c["hp"], c["grad_dtype"]
