@@ -721,11 +721,9 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         // group lies in the normal range (v at least 2^-96 for sqrt_rn; |m|
         // in [2^-40, 2^40] for div_rn, whose divisor sqrt(v) * ibc2 + eps is
         // in [2^-40, 2^77] given ibc2 <= 2^12 and eps in [2^-40, 2^20]) the
-        // wave takes the short sequences, otherwise the general ones.  Same bits either way; one
-        // decision per group lets a group's update start while the next
-        // group's loads are still in flight.  The percentile variants (whose
-        // radix selects dominate) measured faster without the decision and
-        // always take the general sequences.
+        // wave takes the short sequences, otherwise the general ones.  Same
+        // bits either way; one decision per group lets a group's update start
+        // while the next group's loads are still in flight.
         const float(&vden)[kItems] = kAms ? wo : vo;
         const bool in_range = a.fast_ok && v_lo >= 0x1p-96f && m_lo >= 0x1p-40f && m_hi <= 0x1p40f;
         if (__all(in_range)) {
