@@ -52,8 +52,10 @@
  * "flat index" range); blocks of 2048 elements are numbered tensor-major,
  * one fp32 scale per block per quantized moment.  Padding entries stay 0.
  *
- * Threading: calls on one state must be ordered (same stream, or the caller
- * synchronizes); different states are independent.  All device work is
+ * Threading: calls on one state must not run concurrently from several host
+ * threads (they share its host-side table cache) and must be ordered on the
+ * device (same stream, or the caller synchronizes); different states are
+ * independent, from any threads and streams.  All device work is
  * enqueued on the caller's HIP stream (hipStream_t passed as void*; NULL is
  * the null stream); argument errors are reported synchronously before any
  * device work.  adam_last_error() returns a thread-local message for the
