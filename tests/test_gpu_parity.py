@@ -273,6 +273,48 @@ def test_mixed_magnitudes_in_one_block(storage, eps):
     st.destroy()
 
 
+@pytest.mark.parametrize("storage,ams,static", [("q8", False, False), ("q8", True, False),
+                                                ("q8_v_only", True, False), ("q8", False, True)])
+def test_stochastic_rounding_across_the_folded_quantizer_range(storage, ams, static):
+    # stochastic rounding folds the 2^16 scaling into the block reciprocal
+    # r = qmax / A where r is 0 or in (1/2, 2^100]; blocks here put r on both
+    # sides of both limits (moments up to ~300, scales near 2^-101, v near
+    # 2 * 255) and hold subnormal moments beside large ones, where an unfolded
+    # product rounds to zero: every code must still match the oracle's
+    numels = [2048 * 6, 1000]
+    rng = np.random.default_rng(77)
+    log(f"folded quantizer range {storage} amsgrad={ams} static={static}")
+    params = workloads.host_params(33, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, storage, "f32", amsgrad=ams)
+    ost = oracle.OracleState(numels, storage, amsgrad=ams)
+    hp = dict(HP, stochastic=True, seed=99, static_scales=static)
+    stats = Stats()
+    for t in range(1, 6):
+        grads = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for n in numels]
+        g = grads[0]
+        g[2048:2048 + 8] = 3000.0 * rng.choice([-1.0, 1.0], 8)  # A_m ~ 300, A_v ~ 9000: r < 1/2
+        g[2048 + 100:2048 + 140] = np.float32(1e-44)           # subnormal m beside them
+        g[2048 + 300:2048 + 340] = np.float32(3e-21)           # subnormal v
+        g[4096:6144] = (rng.standard_normal(2048) * 1e-30).astype(np.float32)  # A_m ~ 2^-101: r > 2^100
+        g[6144:6144 + 4] = 700.0                               # A_m ~ 70, A_v ~ 490: r just above 1/2
+        g[6144 + 10:6144 + 60] = np.float32(1e-44)
+        g[6144 + 60:6144 + 110] = np.float32(3e-21)
+        g[8192:8192 + 4] = 714.0                               # A_v ~ 510: r near 1/2
+        g[8192 + 10:8192 + 60] = np.float32(-1e-44)
+        g[10240:12288] = np.float32(0.0)                       # zero block: r = 0
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t} tensor {k}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, True, stats, f"t={t}")
+    log(f"  {stats}")
+    st.destroy()
+
+
 def _random_case(i):
     rng = np.random.default_rng([4242, i])
     storage = ["bf16", "q8", "q8_v_only"][i % 3]
