@@ -30,7 +30,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <type_traits>
 
 #include "adam_internal.h"
 
@@ -85,37 +84,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
 }
 
 // ---------------------------------------------------------------- Philox4x32-10
-// c[2] and c[3] (the step t) are uniform on entry: in the first round the
-// uniform product and its XOR with the key are scalar, and in the second
-// round the word that round left uniform is XORed with the key in scalar
-// code too, so that no vector XOR takes two scalar operands (one scalar
-// operand per VALU instruction here: a second would need a copy into a VGPR).
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
-    {
-        const uint64_t prod0 = (uint64_t)0xD2511F53u * c[0];
-        const uint64_t prod1 = (uint64_t)0xCD9E8D57u * c[2];  // uniform
-        const uint32_t u0 = (uint32_t)(prod1 >> 32) ^ k0;      // uniform
-        const uint32_t u2 = c[3] ^ k1;                         // uniform
-        c[0] = c[1] ^ u0;
-        c[1] = (uint32_t)prod1;                                // uniform
-        c[2] = (uint32_t)(prod0 >> 32) ^ u2;
-        c[3] = (uint32_t)prod0;
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
-    }
-    {
-        const uint64_t prod0 = (uint64_t)0xD2511F53u * c[0];
-        const uint64_t prod1 = (uint64_t)0xCD9E8D57u * c[2];
-        const uint32_t u0 = c[1] ^ k0;                         // uniform
-        c[0] = (uint32_t)(prod1 >> 32) ^ u0;
-        c[1] = (uint32_t)prod1;
-        c[2] = __builtin_amdgcn_bitop3_b32((uint32_t)(prod0 >> 32), c[3], k1, 0x96);
-        c[3] = (uint32_t)prod0;
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
-    }
 #pragma unroll
-    for (int r = 2; r < 10; ++r) {
+    for (int r = 0; r < 10; ++r) {
         // one 32x32->64 multiply each (v_mad_u64_u32) instead of separate hi/lo
         const uint64_t prod0 = (uint64_t)0xD2511F53u * c[0];
         const uint64_t prod1 = (uint64_t)0xCD9E8D57u * c[2];
@@ -462,43 +433,19 @@ __device__ __forceinline__ int32_t cvt_floor(float x) {
     return r;
 }
 
-//
-// kFold (stochastic rounding only): r holds fl(qmax/A) * -2^16, so that one
-// multiply gives -Y.  With fl(qmax/A) in (1/2, 2^100] (fold_ok) the product
-// a * r * -2^16 is the same float as fl(a * fl(qmax/A)) * -2^16: where
-// fl(a * r) is normal, scaling by a power of two commutes with the rounding;
-// where it is subnormal, both products lie in (-1, 0) and floor to -1 (a > 0
-// is at least 2^-149, so a * r exceeds 2^-150 and neither rounds to zero);
-// where a = 0 both are -0.  An overflow to -inf happens at the same a on both
-// sides and is clamped or pinned.  A zero block (r = 0) folds to -0 and gives
-// the same zero codes.
-template <bool kSR, EndRule kEnd, bool kFold = false>
+template <bool kSR, EndRule kEnd>
 __device__ __forceinline__ uint32_t code_magnitude(float a, float A, float r, uint32_t qmax, uint32_t u16) {
+    float y = a * r;
+    if constexpr (kEnd == kClampEnd) y = fminf(y, (float)qmax);
     uint32_t k;
-    if constexpr (kSR && kFold) {
-        float Yn = a * r;  // -Y
-        if constexpr (kEnd == kClampEnd) Yn = fmaxf(Yn, (float)qmax * -65536.0f);
-        k = ((0xFFFFu - u16) - (uint32_t)cvt_floor(Yn)) >> 16;
+    if constexpr (kSR) {
+        // ceil(Y) = -floor(-Y): one convert and one subtract
+        k = ((0xFFFFu - u16) - (uint32_t)cvt_floor(y * -65536.0f)) >> 16;
     } else {
-        float y = a * r;
-        if constexpr (kEnd == kClampEnd) y = fminf(y, (float)qmax);
-        if constexpr (kSR) {
-            // ceil(Y) = -floor(-Y): one convert and one subtract
-            k = ((0xFFFFu - u16) - (uint32_t)cvt_floor(y * -65536.0f)) >> 16;
-        } else {
-            k = (uint32_t)rintf(y);
-        }
+        k = (uint32_t)rintf(y);
     }
     if constexpr (kEnd == kPinEnd) k = a >= A ? qmax : k;
     return k;
-}
-
-// The fold above holds for a block whose r = fl(qmax/A) is 0 or in (1/2,
-// 2^100] (r * 2^16 finite and exact; A below 2 qmax, far above any moment
-// of a training run).  r is block-uniform: compared as bits in scalar code.
-__device__ __forceinline__ bool fold_ok(float r) {
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(r));
-    return b == 0u || (b > 0x3F000000u && b <= 0x71800000u);
 }
 
 // ---------------------------------------------------------------- one block
@@ -681,20 +628,10 @@ __device__ __forceinline__ float div_rn(float n, float d) {
     return fmaf(fmaf(-d, q, n), r, q);
 }
 
-// qmax / A for a block statistic A >= 2^-112: div_rn where A is in its range
-// (qmax = 127 or 255 is), the general sequence otherwise.  A is
-// block-uniform, so the range test is a scalar compare of its bits.
-__device__ __forceinline__ float scale_recip(float qmax, float A) {
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(A));
-    const float Au = __uint_as_float(b);
-    if (b - 0x2B800000u <= 0x66000000u - 0x2B800000u) return div_rn(qmax, Au);  // [2^-40, 2^77]
-    return qmax / Au;
-}
-
 // Codes of four unsigned values x[b..b+3] (v, or the AMSGrad maximum) packed
 // into the bytes of one word; u: the group's four Philox words, of which the
 // 16 bits at `shift` are the draws.
-template <bool kSR, bool kFold>
+template <bool kSR>
 __device__ __forceinline__ uint32_t pack_u8(const float (&x)[kItems], int b, float pin, float r,
                                             const uint32_t (&u)[4], int shift) {
     uint32_t c = 0;
@@ -702,7 +639,7 @@ __device__ __forceinline__ uint32_t pack_u8(const float (&x)[kItems], int b, flo
     for (int k = 0; k < 4; ++k) {
         const float ax = fabsf(x[b + k]);
         if constexpr (kSR) {
-            c |= code_magnitude<true, kPinEnd, kFold>(ax, pin, r, 255u, (u[k] >> shift) & 0xFFFFu) << (8 * k);
+            c |= code_magnitude<true, kPinEnd>(ax, pin, r, 255u, (u[k] >> shift) & 0xFFFFu) << (8 * k);
         } else {
             // nearest-even rounding, clamped to [0, 255], packed into byte k: the
             // clamp is the end pin (|x| >= A gives y >= 254.99998)
@@ -921,80 +858,51 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         }
         constexpr bool kPin = kSR || kPct != kPctNone || kStatic;
         const bool mzero = !(Amn >= kTiny), vzero = !(Avn >= kTiny), wzero = !(Awn >= kTiny);
-        const float rm = (!kQuantM || mzero) ? 0.0f : scale_recip(127.0f, Amn);
-        const float rv = vzero ? 0.0f : scale_recip(255.0f, Avn);
-        const float rw = (!kAms || wzero) ? 0.0f : scale_recip(255.0f, Awn);
+        const float rm = mzero ? 0.0f : 127.0f / Amn;
+        const float rv = vzero ? 0.0f : 255.0f / Avn;
+        const float rw = (!kAms || wzero) ? 0.0f : 255.0f / Awn;
         // a zero block has r = 0, so y = 0 and every code is 0; its pin
         // threshold is +inf so that the end pin never fires
         const float pin_v = vzero ? __builtin_inff() : Avn;
         const float pin_w = wzero ? __builtin_inff() : Awn;
 
-        // ---- requantize and store codes.  With stochastic rounding, blocks
-        // whose scales pass fold_ok take the folded quantizer (one multiply
-        // fewer per code, the same codes); the test is block-uniform.
-        auto requantize = [&](auto fold_tag) {
-            constexpr bool kFold = decltype(fold_tag)::value;
-            const float sm = kFold ? rm * -65536.0f : rm;
-            const float sv = kFold ? rv * -65536.0f : rv;
-            const float sw = kFold ? rw * -65536.0f : rw;
+        // ---- requantize and store codes
 #pragma unroll
-            for (int j = 0; j < kGroups; ++j) {
-                const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
-                if (!kFull && e0 >= c.npad) continue;
-                const size_t s = c.gidx + e0;
-                uint32_t rnd[4] = {0u, 0u, 0u, 0u}, rnd_w[4] = {0u, 0u, 0u, 0u};
-                if constexpr (kSR) {
-                    // opaque copies of the group's moments: otherwise the
-                    // compiler hoists the compares both variants share above
-                    // the branch, into SGPR pairs that push the Philox key
-                    // schedule out of SGPRs
-#pragma unroll
-                    for (int i = 4 * j; i < 4 * j + 4; ++i) {
-                        asm volatile("" : "+v"(vo[i]));
-                        if constexpr (kQuantM) asm volatile("" : "+v"(mo[i]));
-                        if constexpr (kAms) asm volatile("" : "+v"(wo[i]));
-                    }
-                    const uint64_t grp = (c.didx + e0) >> 2;  // draw index / 4
-                    uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), a.t_lo, a.t_hi};
-                    philox4x32_10(ctr, a.seed_lo, a.seed_hi);
-                    rnd[0] = ctr[0]; rnd[1] = ctr[1]; rnd[2] = ctr[2]; rnd[3] = ctr[3];
-                    if constexpr (kAms) {
-                        // the maximum's draws: the counter stream with bit 63 set
-                        uint32_t ctr_w[4] = {(uint32_t)grp, (uint32_t)(grp >> 32) | 0x80000000u,
-                                             a.t_lo, a.t_hi};
-                        philox4x32_10(ctr_w, a.seed_lo, a.seed_hi);
-                        rnd_w[0] = ctr_w[0]; rnd_w[1] = ctr_w[1]; rnd_w[2] = ctr_w[2]; rnd_w[3] = ctr_w[3];
-                    }
-                }
-                st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s,
-                       pack_u8<kSR, kFold>(vo, 4 * j, pin_v, sv, rnd, 16));
-                if constexpr (kAms)
-                    st_u32(reinterpret_cast<uint8_t *>(a.w_state) + s,
-                           pack_u8<kSR, kFold>(wo, 4 * j, pin_w, sw, rnd_w, 0));
-                if constexpr (kQuantM) {
-                    uint32_t cm = 0;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float x = mo[4 * j + k];
-                        const uint32_t q = code_magnitude<kSR, kPin ? kClampEnd : kNoEnd, kFold>(
-                            fabsf(x), Amn, sm, 127u, rnd[k] & 0xFFFFu);
-                        const uint32_t qs = x < 0.0f ? 0u - q : q;  // -0 gives 0
-                        cm |= (qs & 0xFFu) << (8 * k);
-                    }
-                    st_u32(reinterpret_cast<int8_t *>(a.m_state) + s, cm);
-                } else {
-                    st_f32x4(reinterpret_cast<float *>(a.m_state) + s,
-                             f32x4{mo[4 * j], mo[4 * j + 1], mo[4 * j + 2], mo[4 * j + 3]});
+        for (int j = 0; j < kGroups; ++j) {
+            const uint32_t e0 = j * (kThreads * 4) + 4 * tid;
+            if (!kFull && e0 >= c.npad) continue;
+            const size_t s = c.gidx + e0;
+            uint32_t rnd[4] = {0u, 0u, 0u, 0u}, rnd_w[4] = {0u, 0u, 0u, 0u};
+            if constexpr (kSR) {
+                const uint64_t grp = (c.didx + e0) >> 2;  // draw index / 4
+                uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), a.t_lo, a.t_hi};
+                philox4x32_10(ctr, a.seed_lo, a.seed_hi);
+                rnd[0] = ctr[0]; rnd[1] = ctr[1]; rnd[2] = ctr[2]; rnd[3] = ctr[3];
+                if constexpr (kAms) {
+                    // the maximum's draws: the counter stream with bit 63 set
+                    uint32_t ctr_w[4] = {(uint32_t)grp, (uint32_t)(grp >> 32) | 0x80000000u, a.t_lo, a.t_hi};
+                    philox4x32_10(ctr_w, a.seed_lo, a.seed_hi);
+                    rnd_w[0] = ctr_w[0]; rnd_w[1] = ctr_w[1]; rnd_w[2] = ctr_w[2]; rnd_w[3] = ctr_w[3];
                 }
             }
-        };
-        if constexpr (kSR) {
-            if (fold_ok(rv) && (!kQuantM || fold_ok(rm)) && (!kAms || fold_ok(rw)))
-                requantize(std::true_type{});
-            else
-                requantize(std::false_type{});
-        } else {
-            requantize(std::false_type{});
+            st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s, pack_u8<kSR>(vo, 4 * j, pin_v, rv, rnd, 16));
+            if constexpr (kAms)
+                st_u32(reinterpret_cast<uint8_t *>(a.w_state) + s, pack_u8<kSR>(wo, 4 * j, pin_w, rw, rnd_w, 0));
+            if constexpr (kQuantM) {
+                uint32_t cm = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float x = mo[4 * j + k];
+                    const uint32_t q = code_magnitude<kSR, kPin ? kClampEnd : kNoEnd>(fabsf(x), Amn, rm, 127u,
+                                                                                      rnd[k] & 0xFFFFu);
+                    const uint32_t qs = x < 0.0f ? 0u - q : q;  // -0 gives 0
+                    cm |= (qs & 0xFFu) << (8 * k);
+                }
+                st_u32(reinterpret_cast<int8_t *>(a.m_state) + s, cm);
+            } else {
+                st_f32x4(reinterpret_cast<float *>(a.m_state) + s,
+                         f32x4{mo[4 * j], mo[4 * j + 1], mo[4 * j + 2], mo[4 * j + 3]});
+            }
         }
         // a kept scale is not rewritten: with no statistic there is no
         // barrier between the waves' reads of it and this store

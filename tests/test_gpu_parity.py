@@ -275,15 +275,15 @@ def test_mixed_magnitudes_in_one_block(storage, eps):
 
 @pytest.mark.parametrize("storage,ams,static", [("q8", False, False), ("q8", True, False),
                                                 ("q8_v_only", True, False), ("q8", False, True)])
-def test_stochastic_rounding_across_the_folded_quantizer_range(storage, ams, static):
-    # stochastic rounding folds the 2^16 scaling into the block reciprocal
-    # r = qmax / A where r is 0 or in (1/2, 2^100]; blocks here put r on both
-    # sides of both limits (moments up to ~300, scales near 2^-101, v near
-    # 2 * 255) and hold subnormal moments beside large ones, where an unfolded
-    # product rounds to zero: every code must still match the oracle's
+def test_stochastic_rounding_at_extreme_block_scales(storage, ams, static):
+    # stochastic rounding on blocks whose reciprocal r = qmax / A sits far
+    # from a training run's: moments up to ~1000 (r below 1/2), scales near
+    # 2^-101 (r above 2^100), r near 1/2, a zero block, and subnormal moments
+    # beside large ones (their scaled magnitudes underflow): every code must
+    # match the oracle's, bit for bit
     numels = [2048 * 6, 1000]
     rng = np.random.default_rng(77)
-    log(f"folded quantizer range {storage} amsgrad={ams} static={static}")
+    log(f"stochastic rounding at extreme scales {storage} amsgrad={ams} static={static}")
     params = workloads.host_params(33, numels)
     dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
     st = ma.adam_state_create(numels, storage, "f32", amsgrad=ams)
