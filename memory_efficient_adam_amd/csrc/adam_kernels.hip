@@ -164,47 +164,75 @@ __device__ __forceinline__ void block_max(float (&x)[N], float (*red)[kWaves]) {
     }
 }
 
-// rank-th smallest (0-based) of the block's 2048 keys (8 per thread): LDS
-// radix select over the 31 magnitude bits in digits of 11, 11 and 9 bits.
-// Keys are bit patterns of non-negative floats, whose order they preserve.
-__device__ uint32_t block_select(const uint32_t (&key)[kItems], uint32_t rank, uint32_t *hist,
-                                 uint32_t *scratch) {
+// rank-th smallest (0-based) of the block's 2048 keys (8 per thread) of each
+// of N moments at once: LDS radix select over the 31 magnitude bits in digits
+// of 11, 11 and 9 bits, one histogram per moment, so that the N selects share
+// each pass's four barriers.  Keys are |x| as bit patterns (the order of
+// non-negative floats); act[k] (block-uniform) skips moment k's work.
+template <int N>
+__device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N], uint32_t rank0,
+                               uint32_t (&out)[N], uint32_t (*hist)[kBlock], uint32_t (*scratch)[kWaves + 2]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    (void)lane;
-    uint32_t prefix = 0, pmask = 0;
+    uint32_t prefix[N], rank[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) { prefix[k] = 0u; rank[k] = rank0; }
+    uint32_t pmask = 0;
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 20 : (pass == 1 ? 9 : 0);
         const int bits = pass == 2 ? 9 : 11;
         const int nb = 1 << bits;
         const int per = nb / kThreads;
-        for (int i = tid; i < nb; i += kThreads) hist[i] = 0u;
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            if (act[k])
+                for (int i = tid; i < nb; i += kThreads) hist[k][i] = 0u;
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kItems; ++i)
-            if ((key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & (nb - 1)], 1u);
-        __syncthreads();
-        uint32_t mine = 0;
-        for (int i = 0; i < per; ++i) mine += hist[tid * per + i];
-        uint32_t incl = wave_inclusive_sum(mine);
-        if (lane == 63) scratch[wave] = incl;
-        __syncthreads();
-        for (int w = 0; w < wave; ++w) incl += scratch[w];
-        const uint32_t excl = incl - mine;
-        if (excl <= rank && rank < incl) {
-            uint32_t cum = excl;
-            int b = tid * per;
-            while (cum + hist[b] <= rank) cum += hist[b++];
-            scratch[kWaves] = (uint32_t)b;
-            scratch[kWaves + 1] = rank - cum;
+        for (int k = 0; k < N; ++k) {
+            if (!act[k]) continue;
+#pragma unroll
+            for (int i = 0; i < kItems; ++i) {
+                const uint32_t key = __float_as_uint(x[k][i]) & 0x7FFFFFFFu;
+                if ((key & pmask) == prefix[k]) atomicAdd(&hist[k][(key >> shift) & (nb - 1)], 1u);
+            }
         }
         __syncthreads();
-        const uint32_t digit = scratch[kWaves];
-        rank = scratch[kWaves + 1];
-        prefix |= digit << shift;
+        uint32_t mine[N], incl[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            mine[k] = 0u;
+            incl[k] = 0u;
+            if (!act[k]) continue;
+            for (int i = 0; i < per; ++i) mine[k] += hist[k][tid * per + i];
+            incl[k] = wave_inclusive_sum(mine[k]);
+            if (lane == 63) scratch[k][wave] = incl[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            if (!act[k]) continue;
+            for (int w = 0; w < wave; ++w) incl[k] += scratch[k][w];
+            const uint32_t excl = incl[k] - mine[k];
+            if (excl <= rank[k] && rank[k] < incl[k]) {
+                uint32_t cum = excl;
+                int b = tid * per;
+                while (cum + hist[k][b] <= rank[k]) cum += hist[k][b++];
+                scratch[k][kWaves] = (uint32_t)b;
+                scratch[k][kWaves + 1] = rank[k] - cum;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            if (!act[k]) continue;
+            prefix[k] |= scratch[k][kWaves] << shift;
+            rank[k] = scratch[k][kWaves + 1];
+        }
         pmask |= (uint32_t)(nb - 1) << shift;
     }
-    return prefix;
+#pragma unroll
+    for (int k = 0; k < N; ++k) out[k] = prefix[k];
 }
 
 // The same statistic when it lies near the top: the rank-th smallest of the
@@ -580,19 +608,19 @@ struct BlockLds {
 // the top walks or by the radix select.
 enum PctMode { kPctNone = 0, kPctTop = 1, kPctRadix = 2 };
 
-// LDS of the percentile statistic.
-template <int kPct>
+// LDS of the percentile statistic (kN: moments with a statistic, 2 or 3).
+template <int kPct, int kN>
 struct SelectLds {};
-template <>
-struct SelectLds<kPctTop> {  // wave lists of the walks (m, v, AMSGrad maximum)
+template <int kN>
+struct SelectLds<kPctTop, kN> {  // wave lists of the walks (m, v, AMSGrad maximum)
     uint32_t val[3][kWaves * kTopCap];
     uint32_t cnt[3][kWaves * kTopCap];
     uint32_t res[3];  // merged statistic of each moment
 };
-template <>
-struct SelectLds<kPctRadix> {  // histogram + scan scratch
-    uint32_t h[kBlock];
-    uint32_t s[kWaves + 2];
+template <int kN>
+struct SelectLds<kPctRadix, kN> {  // one histogram + scan scratch per moment
+    uint32_t h[kN][kBlock];
+    uint32_t s[kN][kWaves + 2];
 };
 
 // ---------------------------------------------------------------- exact sqrt / divide
@@ -661,7 +689,7 @@ __device__ __forceinline__ float uniform(float x) {
 template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAms, bool kFull>
 __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx &c,
                                               const BlockRegs<kStore, kGradBf16, kAms> &r,
-                                              BlockLds &lds, SelectLds<kPct> &sel) {
+                                              BlockLds &lds, SelectLds<kPct, kAms ? 3 : 2> &sel) {
     constexpr bool kQuantM = (kStore == kStoreQ8);
     const int tid = threadIdx.x;
     float p[kItems], g[kItems], mo[kItems], vo[kItems], wo[kItems];  // wo: AMSGrad only
@@ -831,30 +859,33 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             __syncthreads();
         }
         if constexpr (kPct != kPctNone) {
-            auto stat = [&](const float (&x)[kItems], int which) -> float {
-                if constexpr (kPct == kPctTop) {
-                    return __uint_as_float(sel.res[which]);
+            float st[3] = {0.0f, 0.0f, 0.0f};
+            if constexpr (kPct == kPctTop) {
+                st[0] = __uint_as_float(sel.res[0]);
+                st[1] = __uint_as_float(sel.res[1]);
+                st[2] = __uint_as_float(sel.res[2]);
+            } else {
+                if constexpr (kAms) {
+                    const float *const xs[3] = {mo, vo, wo};
+                    const bool act[3] = {need_m, need_v, need_w};
+                    uint32_t res[3];
+                    block_select_n<3>(xs, act, rank, res, sel.h, sel.s);
+                    st[0] = __uint_as_float(res[0]);
+                    st[1] = __uint_as_float(res[1]);
+                    st[2] = __uint_as_float(res[2]);
                 } else {
-                    uint32_t key[kItems];
-#pragma unroll
-                    for (int i = 0; i < kItems; ++i) key[i] = __float_as_uint(x[i]) & 0x7FFFFFFFu;
-                    return __uint_as_float(block_select(key, rank, sel.h, sel.s));
-                }
-            };
-            if (need_m) {
-                const float sv = stat(mo, 0);
-                Amn = sv < kTiny ? mmax : sv;
-            }
-            if (need_v) {
-                const float sv = stat(vo, 1);
-                Avn = sv < kTiny ? vmax : sv;
-            }
-            if constexpr (kAms) {
-                if (need_w) {
-                    const float sv = stat(wo, 2);
-                    Awn = sv < kTiny ? wmax : sv;
+                    const float *const xs[2] = {mo, vo};
+                    const bool act[2] = {need_m, need_v};
+                    uint32_t res[2];
+                    block_select_n<2>(xs, act, rank, res, sel.h, sel.s);
+                    st[0] = __uint_as_float(res[0]);
+                    st[1] = __uint_as_float(res[1]);
                 }
             }
+            if (need_m) Amn = st[0] < kTiny ? mmax : st[0];
+            if (need_v) Avn = st[1] < kTiny ? vmax : st[1];
+            if constexpr (kAms)
+                if (need_w) Awn = st[2] < kTiny ? wmax : st[2];
         }
         constexpr bool kPin = kSR || kPct != kPctNone || kStatic;
         const bool mzero = !(Amn >= kTiny), vzero = !(Avn >= kTiny), wzero = !(Awn >= kTiny);
@@ -921,7 +952,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAms>
 __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
     __shared__ BlockLds lds;
-    __shared__ SelectLds<kPct> sel;
+    __shared__ SelectLds<kPct, kAms ? 3 : 2> sel;
     for (uint32_t i0 = blockIdx.x; i0 < a.n_all; i0 += gridDim.x) {
         // XCD-aware order: workgroup i0 runs on XCD i0 mod 8, and here each
         // XCD takes runs of 16 consecutive blocks, the runs dealt round-robin
@@ -968,7 +999,7 @@ hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     const uint32_t grid = std::min<uint32_t>(a.n_all, kMaxGrid);
     if (grid == 0) return hipSuccess;
     constexpr int kResident = kStore == kStoreBf16 ? ADAM_BF16_RESIDENT_PER_CU : ADAM_Q8_RESIDENT_PER_CU;
-    constexpr size_t kStaticLds = sizeof(BlockLds) + sizeof(SelectLds<kPct>);
+    constexpr size_t kStaticLds = sizeof(BlockLds) + sizeof(SelectLds<kPct, kAms ? 3 : 2>);
     constexpr size_t kDyn = reserve_lds(kResident) > kStaticLds ? reserve_lds(kResident) - kStaticLds : 0;
     hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct, kStatic, kAms>), dim3(grid), dim3(kThreads),
                        kDyn, stream, a);
