@@ -194,9 +194,11 @@ def main():
 
     alg = algorithmic_bytes(cfg)
     achieved = alg / sec / 1e9
-    # counter readings are taken per workload for its own kernel variant
-    variant_changed = args.static_scales or cfg.amsgrad or args.percentile is not None
-    traffic = None if variant_changed else traffic_for(cfg.name)
+    # counter readings are taken per workload for its own kernel variant (a
+    # percentile run of an 8-bit set has its own record when one was taken)
+    variant_changed = args.static_scales or cfg.amsgrad
+    key = cfg.name if args.percentile is None else f"{cfg.name}_percentile{args.percentile}"
+    traffic = None if variant_changed else traffic_for(key)
     out = {
         "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",
         "value": round(n_params / sec / 1e9, 3),
