@@ -138,6 +138,40 @@ def test_static_scales_set_late_and_mixed_with_dynamic_steps(storage):
     st.destroy()
 
 
+@pytest.mark.parametrize("ams", [False, True])
+@pytest.mark.parametrize("pct", [99.0, 50.0])
+def test_static_scales_radix_select_with_one_moment_kept(ams, pct):
+    # the radix select runs the moments' selects side by side; with static
+    # scales a block may keep one moment's scale while another still needs
+    # its statistic: tiny gradients (1e-20) give tensor 1 a first-moment
+    # scale at step 1 while its v underflows (no scale) until step 4, and
+    # tensor 2 starts from zero gradients (no scale for either)
+    numels = RAGGED
+    log(f"static scales, radix percentile {pct}, one moment kept, amsgrad={ams}")
+    params = workloads.host_params(16, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, "q8", "f32", amsgrad=ams)
+    ost = oracle.OracleState(numels, "q8", amsgrad=ams)
+    stats = Stats()
+    for t in range(1, 7):
+        grads = workloads.host_grads(16, numels, t)
+        if t <= 3:
+            grads[1] = (grads[1] * np.float32(1e-17)).astype(np.float32)
+        if t <= 2:
+            grads[2] = np.zeros_like(grads[2])
+        hp = dict(HP, static_scales=True, percentile=pct, stochastic=(t % 2 == 0), seed=17)
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t} tensor {k}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, hp["stochastic"], stats, f"t={t}")
+    log(f"  {stats}")
+    st.destroy()
+
+
 # percentiles whose full-block rank lands near the top: need = 2048 - rank
 # keys at or above the statistic, with rank = floor(p/100 * 2047).  Up to
 # 16 the kernel walks down the top values per wave, beyond it it takes the
