@@ -122,6 +122,8 @@ def main():
                     help="keep the running maximum of v (AMSGrad)")
     ap.add_argument("--percentile", type=float, default=None,
                     help="8-bit sets: percentile block statistic (e.g. 99.9) instead of the set's own")
+    ap.add_argument("--nearest", action="store_true",
+                    help="8-bit sets: nearest-even rounding instead of the set's stochastic rounding")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's device copy of 4 GiB (counter calibration run)")
     args = ap.parse_args()
@@ -163,6 +165,10 @@ def main():
         if cfg.storage == "bf16":
             sys.exit("bench.py: --static-scales applies to 8-bit storage only")
         hp["static_scales"] = True
+    if args.nearest:
+        if cfg.storage == "bf16":
+            sys.exit("bench.py: --nearest applies to 8-bit storage only")
+        hp["stochastic"] = False
     if args.percentile is not None:
         if cfg.storage == "bf16":
             sys.exit("bench.py: --percentile applies to 8-bit storage only")
@@ -197,7 +203,8 @@ def main():
     # counter readings are taken per workload for its own kernel variant (a
     # percentile run of an 8-bit set has its own record when one was taken)
     variant_changed = args.static_scales or cfg.amsgrad
-    key = cfg.name if args.percentile is None else f"{cfg.name}_percentile{args.percentile}"
+    key = cfg.name + ("_nearest" if args.nearest else "") + (
+        "" if args.percentile is None else f"_percentile{args.percentile}")
     traffic = None if variant_changed else traffic_for(key)
     out = {
         "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",

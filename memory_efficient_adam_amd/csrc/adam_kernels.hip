@@ -978,15 +978,21 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
     }
 }
 
-// Occupancy cap.  Too many outstanding requests thrash the HBM pages: with
-// bf16 moments (no block statistic, short compute) the step streams fastest
-// with at most 3 workgroups resident per CU, so that launch reserves LDS it
-// does not use (CU LDS is 160 KiB).  The 8-bit variants spend longer per
-// block (statistic, requantization) and need every resident workgroup to
-// keep enough bytes in flight, so they are not capped.
+// Occupancy cap.  Too many outstanding requests thrash the HBM pages, so the
+// variants with little compute per block stream fastest with few workgroups
+// resident per CU; their launch reserves LDS it does not use (CU LDS is 160
+// KiB).  Measured per variant: bf16 moments (no block statistic) at most 3;
+// 8-bit with the block maximum and nearest rounding at most 4 (GPT-1.3B
+// shaped set with bf16 gradients +7% over uncapped, ViT-Base with fp32
+// gradients unchanged).  Stochastic rounding and the percentile statistics
+// spend longer per block and need every resident workgroup to keep enough
+// bytes in flight (a cap of 4 cost them 5-7%), so they are not capped.
 constexpr int kCuLdsBytes = 160 * 1024;
 #ifndef ADAM_BF16_RESIDENT_PER_CU
 #define ADAM_BF16_RESIDENT_PER_CU 3
+#endif
+#ifndef ADAM_Q8_NEAREST_RESIDENT_PER_CU
+#define ADAM_Q8_NEAREST_RESIDENT_PER_CU 4
 #endif
 #ifndef ADAM_Q8_RESIDENT_PER_CU
 #define ADAM_Q8_RESIDENT_PER_CU 8
@@ -998,7 +1004,9 @@ template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAm
 hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     const uint32_t grid = std::min<uint32_t>(a.n_all, kMaxGrid);
     if (grid == 0) return hipSuccess;
-    constexpr int kResident = kStore == kStoreBf16 ? ADAM_BF16_RESIDENT_PER_CU : ADAM_Q8_RESIDENT_PER_CU;
+    constexpr int kResident = kStore == kStoreBf16                ? ADAM_BF16_RESIDENT_PER_CU
+                              : (!kSR && kPct == kPctNone) ? ADAM_Q8_NEAREST_RESIDENT_PER_CU
+                                                             : ADAM_Q8_RESIDENT_PER_CU;
     constexpr size_t kStaticLds = sizeof(BlockLds) + sizeof(SelectLds<kPct, kAms ? 3 : 2>);
     constexpr size_t kDyn = reserve_lds(kResident) > kStaticLds ? reserve_lds(kResident) - kStaticLds : 0;
     hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct, kStatic, kAms>), dim3(grid), dim3(kThreads),
