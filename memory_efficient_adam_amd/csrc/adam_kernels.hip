@@ -215,10 +215,22 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
             for (int w = 0; w < wave; ++w) incl[k] += scratch[k][w];
             const uint32_t excl = incl[k] - mine[k];
             if (excl <= rank[k] && rank[k] < incl[k]) {
-                uint32_t cum = excl;
-                int b = tid * per;
-                while (cum + hist[k][b] <= rank[k]) cum += hist[k][b++];
-                scratch[k][kWaves] = (uint32_t)b;
+                // the digit is among this thread's bins: read them at once and
+                // take the first whose running count passes the rank (no chain
+                // of dependent LDS reads while the other waves wait)
+                uint32_t hb[kBlock / kThreads];
+#pragma unroll
+                for (int i = 0; i < kBlock / kThreads; ++i) hb[i] = i < per ? hist[k][tid * per + i] : 0u;
+                uint32_t cum = excl, b = (uint32_t)(tid * per);
+                bool found = false;
+#pragma unroll
+                for (int i = 0; i < kBlock / kThreads; ++i) {
+                    const bool take = !found && i < per && cum + hb[i] <= rank[k];
+                    cum = take ? cum + hb[i] : cum;
+                    b += take ? 1u : 0u;
+                    found = found || !take;
+                }
+                scratch[k][kWaves] = b;
                 scratch[k][kWaves + 1] = rank[k] - cum;
             }
         }
