@@ -184,9 +184,16 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
         const int nb = 1 << bits;
         const int per = nb / kThreads;
 #pragma unroll
-        for (int k = 0; k < N; ++k)
-            if (act[k])
-                for (int i = tid; i < nb; i += kThreads) hist[k][i] = 0u;
+        for (int k = 0; k < N; ++k) {
+            if (!act[k]) continue;
+            // this thread's `per` adjacent bins, in 16-byte stores
+            uint4 *h4 = reinterpret_cast<uint4 *>(&hist[k][tid * per]);
+#pragma unroll
+            for (int i = 0; i < kBlock / kThreads / 4; ++i)
+                if (4 * i + 4 <= per) h4[i] = uint4{0u, 0u, 0u, 0u};
+            if (per < 4)
+                for (int i = 0; i < per; ++i) hist[k][tid * per + i] = 0u;
+        }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < N; ++k) {
@@ -631,7 +638,7 @@ struct SelectLds<kPctTop, kN> {  // wave lists of the walks (m, v, AMSGrad maxim
 };
 template <int kN>
 struct SelectLds<kPctRadix, kN> {  // one histogram + scan scratch per moment
-    uint32_t h[kN][kBlock];
+    alignas(16) uint32_t h[kN][kBlock];  // 16-byte aligned rows: cleared in 16-byte stores
     uint32_t s[kN][kWaves + 2];
 };
 
