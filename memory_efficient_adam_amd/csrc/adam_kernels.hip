@@ -1003,9 +1003,12 @@ __global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
 // KiB).  Measured per variant: bf16 moments (no block statistic) at most 3;
 // 8-bit with the block maximum and nearest rounding at most 4 (GPT-1.3B
 // shaped set with bf16 gradients +7% over uncapped, ViT-Base with fp32
-// gradients unchanged).  Stochastic rounding and the percentile statistics
-// spend longer per block and need every resident workgroup to keep enough
-// bytes in flight (a cap of 4 cost them 5-7%), so they are not capped.
+// gradients unchanged); fp32 m + 8-bit v with the percentile walk and
+// nearest rounding (one walk per block) at most 4 (Llama-7B shaped set
+// +2.6%).  Stochastic rounding, the radix select and the walks over two or
+// three moments spend longer per block and need every resident workgroup to
+// keep enough bytes in flight (a cap of 4 cost them 5-9%), so they are not
+// capped.
 constexpr int kCuLdsBytes = 160 * 1024;
 #ifndef ADAM_BF16_RESIDENT_PER_CU
 #define ADAM_BF16_RESIDENT_PER_CU 3
@@ -1023,9 +1026,10 @@ template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAm
 hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     const uint32_t grid = std::min<uint32_t>(a.n_all, kMaxGrid);
     if (grid == 0) return hipSuccess;
-    constexpr int kResident = kStore == kStoreBf16                ? ADAM_BF16_RESIDENT_PER_CU
-                              : (!kSR && kPct == kPctNone) ? ADAM_Q8_NEAREST_RESIDENT_PER_CU
-                                                             : ADAM_Q8_RESIDENT_PER_CU;
+    constexpr bool kLight = !kSR && (kPct == kPctNone || (kPct == kPctTop && kStore == kStoreQ8VOnly && !kAms));
+    constexpr int kResident = kStore == kStoreBf16 ? ADAM_BF16_RESIDENT_PER_CU
+                              : kLight             ? ADAM_Q8_NEAREST_RESIDENT_PER_CU
+                                                   : ADAM_Q8_RESIDENT_PER_CU;
     constexpr size_t kStaticLds = sizeof(BlockLds) + sizeof(SelectLds<kPct, kAms ? 3 : 2>);
     constexpr size_t kDyn = reserve_lds(kResident) > kStaticLds ? reserve_lds(kResident) - kStaticLds : 0;
     hipLaunchKernelGGL((adam_step_kernel<kStore, kGradBf16, kSR, kPct, kStatic, kAms>), dim3(grid), dim3(kThreads),
