@@ -50,7 +50,9 @@
  * State layout (device memory owned by the library): tensor k's segment has
  * pad16(numel_k) entries and starts at the sum of the earlier segments (its
  * "flat index" range); blocks of 2048 elements are numbered tensor-major,
- * one fp32 scale per block per quantized moment.  Padding entries stay 0.
+ * one fp32 scale per block per quantized moment.  Padding entries take no
+ * part in a step (whatever they hold decodes as zero) and a step stores
+ * them back as zero.
  *
  * Threading: calls on one state must not run concurrently from several host
  * threads (they share its host-side table cache) and must be ordered on the

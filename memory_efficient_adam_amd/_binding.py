@@ -106,6 +106,47 @@ def _numels(numels):
     return len(numels), arr
 
 
+def _current_device():
+    import torch
+    return torch.cuda.current_device()
+
+
+_GRAD_TORCH_DTYPES = {0: ("float32",), 1: ("bfloat16", "int16", "uint16")}
+
+
+def _check_step_tensors(state, params, grads):
+    """The kernel reads and writes exactly numel elements through each raw
+    pointer: a shorter, strided, mistyped or host tensor would make it touch
+    memory that is not the tensor's.  Every tensor is checked here, before
+    any pointer reaches the library."""
+    import torch
+    n = len(state.numels)
+    if len(params) != n or len(grads) != n:
+        raise ValueError(f"expected {n} params and grads, got {len(params)} and {len(grads)}")
+    gdts = _GRAD_TORCH_DTYPES[state.layout.grad_dtype]
+    for k, (p, g, want) in enumerate(zip(params, grads, state.numels)):
+        if not isinstance(p, torch.Tensor) or not isinstance(g, torch.Tensor):
+            raise TypeError(f"tensor {k}: params and grads must be torch tensors")
+        if p.dtype != torch.float32:
+            raise ValueError(f"param {k}: dtype {p.dtype}, expected torch.float32")
+        if str(g.dtype).replace("torch.", "") not in gdts:
+            raise ValueError(f"grad {k}: dtype {g.dtype}, expected one of {gdts} for this layout")
+        if p.numel() != want or g.numel() != want:
+            raise ValueError(f"tensor {k}: param/grad numel {p.numel()}/{g.numel()}, the state "
+                             f"holds {want}")
+        if not p.is_contiguous() or not g.is_contiguous():
+            raise ValueError(f"tensor {k}: params and grads must be contiguous")
+    for k, (p, g, want) in enumerate(zip(params, grads, state.numels)):
+        if want == 0:
+            continue
+        if not p.is_cuda or not g.is_cuda:
+            raise ValueError(f"tensor {k}: params and grads must be CUDA (HIP) device tensors")
+        if state.device is not None and (p.device.index != state.device
+                                         or g.device.index != state.device):
+            raise ValueError(f"tensor {k}: on {p.device}/{g.device}, the state lives on "
+                             f"cuda:{state.device}")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -126,12 +167,14 @@ def adam_state_bytes(numels, storage, grad_dtype="f32", block_size=ADAM_BLOCK_SI
 
 
 class AdamState:
-    """Owns one library state (freed on destroy() or garbage collection)."""
+    """Owns one library state (freed on destroy() or garbage collection).
+    device: the CUDA device index the state lives on (None: not recorded)."""
 
-    def __init__(self, handle, numels, layout):
+    def __init__(self, handle, numels, layout, device=None):
         self.handle = handle
         self.numels = list(numels)
         self.layout = layout
+        self.device = device
 
     def __del__(self):
         self.destroy()
@@ -159,7 +202,7 @@ def adam_state_create(numels, storage, grad_dtype="f32", block_size=ADAM_BLOCK_S
     h = ctypes.c_void_p()
     _check(library().adam_state_create(ctypes.byref(h), n, arr, ctypes.byref(lay),
                                        _stream(stream)))
-    return AdamState(h.value, numels, lay)
+    return AdamState(h.value, numels, lay, _current_device())
 
 
 def adam_state_destroy(state):
@@ -174,20 +217,25 @@ def adam_step(state, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
     absmax block statistic; static_scales keeps each block's scale once set.
     expect: (storage, grad_dtype[, block_size[, options]]) the caller believes
     the state has (default: the state's own layout)."""
+    _check_step_tensors(state, params, grads)
     n = len(state.numels)
-    if len(params) != n or len(grads) != n:
-        raise ValueError(f"expected {n} params and grads")
     P = (ctypes.c_void_p * max(n, 1))(*[p.data_ptr() for p in params])
     G = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
-    flags = ((_F_DECOUPLED if decoupled else 0) | (_F_STOCHASTIC if stochastic else 0)
-             | (_F_PERCENTILE if percentile is not None else 0)
-             | (_F_STATIC_SCALES if static_scales else 0))
-    hp = adam_hparams(lr, beta1, beta2, eps, weight_decay,
-                      100.0 if percentile is None else percentile, int(t), flags, 0, int(seed))
+    hp = _hparams(lr, beta1, beta2, eps, weight_decay, t, decoupled, stochastic, percentile, seed,
+                  static_scales)
     lay = state.layout if expect is None else _layout(*expect)
     _check(library().adam_step(state.handle, ctypes.cast(P, ctypes.c_void_p),
                                ctypes.cast(G, ctypes.c_void_p), ctypes.byref(hp),
                                ctypes.byref(lay), _stream(stream)))
+
+
+def _hparams(lr, beta1, beta2, eps, weight_decay, t, decoupled, stochastic, percentile, seed,
+             static_scales):
+    flags = ((_F_DECOUPLED if decoupled else 0) | (_F_STOCHASTIC if stochastic else 0)
+             | (_F_PERCENTILE if percentile is not None else 0)
+             | (_F_STATIC_SCALES if static_scales else 0))
+    return adam_hparams(lr, beta1, beta2, eps, weight_decay,
+                        100.0 if percentile is None else percentile, int(t), flags, 0, int(seed))
 
 
 def adam_state_buffer_bytes(state, which):
@@ -211,6 +259,9 @@ def adam_state_read(state, which, out=None, stream=None):
     if out is None:
         dt = getattr(torch, _BUF_DTYPES[which])
         out = torch.empty(nbytes // dt.itemsize, dtype=dt, device="cuda")
+    elif out.numel() * out.element_size() != nbytes or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous tensor of exactly {nbytes} bytes, got "
+                         f"{out.numel() * out.element_size()} bytes")
     _check(library().adam_state_read(state.handle, BUFFERS[which], out.data_ptr(), nbytes,
                                      _stream(stream)))
     return out
@@ -218,8 +269,9 @@ def adam_state_read(state, which, out=None, stream=None):
 
 def adam_state_write(state, which, src, stream=None):
     nbytes = adam_state_buffer_bytes(state, which)
-    if src.numel() * src.element_size() != nbytes:
-        raise ValueError("size mismatch")
+    if src.numel() * src.element_size() != nbytes or not src.is_contiguous():
+        raise ValueError(f"src must be a contiguous tensor of exactly {nbytes} bytes, got "
+                         f"{src.numel() * src.element_size()} bytes")
     _check(library().adam_state_write(state.handle, BUFFERS[which], src.data_ptr(), nbytes,
                                       _stream(stream)))
 
@@ -276,6 +328,6 @@ def adam_state_load(buf, stream=None):
                                else buf.view(np.uint8))
     h = ctypes.c_void_p()
     _check(library().adam_state_load(ctypes.byref(h), arr.ctypes.data, arr.size, _stream(stream)))
-    st = AdamState(h.value, [], adam_layout())
+    st = AdamState(h.value, [], adam_layout(), _current_device())
     st.layout, st.numels = adam_state_describe(st)
     return st

@@ -736,6 +736,21 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             }
         }
     }
+    if constexpr (!kFull) {
+        // State entries past the tensor's end (its 16-element padding) take
+        // no part in the step: whatever a written or loaded state holds
+        // there decodes as zero, so the block statistic sees the live
+        // elements and zeros only, and the padding is stored back as zero.
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) {
+            const uint32_t e = (i / 4) * (kThreads * 4) + 4 * tid + (i & 3);
+            if (e >= c.n) {
+                mo[i] = 0.0f;
+                vo[i] = 0.0f;
+                if constexpr (kAms) wo[i] = 0.0f;
+            }
+        }
+    }
 
     // ---- the Adam/AdamW element update (moments stay in registers)
     if (a.l2) {  // Adam with L2-coupled weight decay (uniform branch)

@@ -233,6 +233,31 @@ BufferView buffer_of(const adam_state *s, int32_t which) {
     }
 }
 
+// The per-step arguments of the kernel from hyperparameters (fp64 host
+// scalars, each rounded once), shared by both step entry points.
+void fill_scalars(StepArgs &a, const adam_hparams *hp) {
+    const double b1 = hp->beta1, b2 = hp->beta2;
+    const double bc1 = 1.0 - std::pow(b1, (double)hp->t);
+    const double bc2 = 1.0 - std::pow(b2, (double)hp->t);
+    const bool decoupled = (hp->flags & ADAM_F_DECOUPLED_WD) != 0;
+    a.step = (float)((double)hp->lr / bc1);
+    a.ibc2 = (float)(1.0 / std::sqrt(bc2));
+    a.decay = decoupled ? (float)(1.0 - (double)hp->lr * (double)hp->weight_decay) : 1.0f;
+    a.omb1 = (float)(1.0 - b1);
+    a.omb2 = (float)(1.0 - b2);
+    a.beta1 = hp->beta1;
+    a.beta2 = hp->beta2;
+    a.eps = hp->eps;
+    a.wd = hp->weight_decay;
+    a.l2 = decoupled ? 0u : 1u;
+    a.fast_ok = (hp->eps >= 0x1p-40f && hp->eps <= 0x1p20f) ? 1u : 0u;
+    a.pfrac = (double)hp->percentile / 100.0;
+    a.seed_lo = (uint32_t)hp->seed;
+    a.seed_hi = (uint32_t)(hp->seed >> 32);
+    a.t_lo = (uint32_t)(uint64_t)hp->t;
+    a.t_hi = (uint32_t)((uint64_t)hp->t >> 32);
+}
+
 }  // namespace
 
 extern "C" {
@@ -719,11 +744,6 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
         }
         s->tables[slot].last_use = ++s->table_clock;
 
-        // host scalars: fp64, each rounded once to fp32
-        const double b1 = hp->beta1, b2 = hp->beta2;
-        const double bc1 = 1.0 - std::pow(b1, (double)hp->t);
-        const double bc2 = 1.0 - std::pow(b2, (double)hp->t);
-        const bool decoupled = (hp->flags & ADAM_F_DECOUPLED_WD) != 0;
         StepArgs a{};
         a.desc = s->d_desc;
         a.tensors = s->tables[slot].dev;
@@ -734,22 +754,7 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
         a.draw_first = s->d_draw;
         a.w_state = s->w;
         a.w_scale = s->w_scale;
-        a.step = (float)((double)hp->lr / bc1);
-        a.ibc2 = (float)(1.0 / std::sqrt(bc2));
-        a.decay = decoupled ? (float)(1.0 - (double)hp->lr * (double)hp->weight_decay) : 1.0f;
-        a.omb1 = (float)(1.0 - b1);
-        a.omb2 = (float)(1.0 - b2);
-        a.beta1 = hp->beta1;
-        a.beta2 = hp->beta2;
-        a.eps = hp->eps;
-        a.wd = hp->weight_decay;
-        a.l2 = decoupled ? 0u : 1u;
-        a.fast_ok = (hp->eps >= 0x1p-40f && hp->eps <= 0x1p20f) ? 1u : 0u;
-        a.pfrac = (double)hp->percentile / 100.0;
-        a.seed_lo = (uint32_t)hp->seed;
-        a.seed_hi = (uint32_t)(hp->seed >> 32);
-        a.t_lo = (uint32_t)(uint64_t)hp->t;
-        a.t_hi = (uint32_t)((uint64_t)hp->t >> 32);
+        fill_scalars(a, hp);  // host scalars: fp64, each rounded once to fp32
 
         a.n_full = (uint32_t)s->n_full;
         a.n_all = (uint32_t)s->nblocks;

@@ -241,3 +241,62 @@ def test_load_of_a_valid_stream_gets_past_validation(storage, options, draw):
         ma.library().adam_state_destroy(h)
     else:
         assert rc in (-4, -5), ma.adam_last_error()
+
+
+# ---------------------------------------------------------------- binding checks
+# The torch-facing binding hands raw pointers to the kernel, which reads and
+# writes numel elements through each; every tensor is checked before any
+# library call (these run with no GPU and no library state).
+def _fake_state(numels, grad_dtype=0):
+    return B.AdamState(None, numels, B.adam_layout(2, grad_dtype, 2048, 0), device=0)
+
+
+def test_step_rejects_bad_tensors_before_any_call():
+    import torch
+    st = _fake_state([100, 7])
+    ok_p = [torch.zeros(100), torch.zeros(7)]
+    ok_g = [torch.zeros(100), torch.zeros(7)]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, t=1)
+    bad_cases = [
+        ([torch.zeros(100)], ok_g, "expected 2"),                                # count
+        ([torch.zeros(99), torch.zeros(7)], ok_g, "numel"),                      # short param
+        (ok_p, [torch.zeros(100), torch.zeros(8)], "numel"),                     # long grad
+        ([torch.zeros(100, dtype=torch.float64), torch.zeros(7)], ok_g, "dtype"),
+        (ok_p, [torch.zeros(100, dtype=torch.bfloat16), torch.zeros(7)], "dtype"),
+        ([torch.zeros(200)[::2], torch.zeros(7)], ok_g, "contiguous"),           # strided view
+        (ok_p, ok_g, "device"),                                                  # host tensors
+    ]
+    for params, grads, what in bad_cases:
+        with pytest.raises(ValueError, match=what):
+            ma.adam_step(st, params, grads, **hp)
+    with pytest.raises(TypeError):
+        ma.adam_step(st, [None, torch.zeros(7)], ok_g, **hp)
+    # bf16 gradients for a bf16-gradient layout: fp32 ones are refused
+    st16 = _fake_state([100], grad_dtype=1)
+    with pytest.raises(ValueError, match="dtype"):
+        ma.adam_step(st16, [torch.zeros(100)], [torch.zeros(100)], **hp)
+    with pytest.raises(ValueError, match="device"):  # right dtype, still host memory
+        ma.adam_step(st16, [torch.zeros(100)], [torch.zeros(100, dtype=torch.bfloat16)], **hp)
+    # zero-size tensors carry no pointer the kernel uses
+    st0 = _fake_state([0])
+    with pytest.raises(ma.AdamError):  # reaches the library, which refuses a NULL state
+        ma.adam_step(st0, [torch.zeros(0)], [torch.zeros(0)], stream=0, **hp)
+
+
+def test_state_read_write_reject_wrong_sizes():
+    import torch
+    st = _fake_state([100])
+    # buffer sizes come from the library: a NULL state fails there first, so
+    # check the size rule through a stand-in that reports 112 bytes
+    orig = B.adam_state_buffer_bytes
+    B.adam_state_buffer_bytes = lambda state, which: 112
+    try:
+        with pytest.raises(ValueError, match="112 bytes"):
+            ma.adam_state_read(st, "v_codes", out=torch.empty(100, dtype=torch.uint8))
+        with pytest.raises(ValueError, match="112 bytes"):
+            ma.adam_state_read(st, "v_codes", out=torch.empty(224, dtype=torch.uint8)[::2])
+        with pytest.raises(ValueError, match="112 bytes"):
+            ma.adam_state_write(st, "v_codes", torch.empty(111, dtype=torch.uint8))
+    finally:
+        B.adam_state_buffer_bytes = orig
+

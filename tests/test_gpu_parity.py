@@ -678,15 +678,33 @@ def test_step_from_injected_state(storage, ams):
             buf[:] = oracle.bf16_from_f32(x if name == "m_bf16" else np.abs(x))
         elif name == "m_f32":
             buf[:] = (rng.standard_normal(buf.size) * 1e-3).astype(np.float32)
-    # padding entries stay zero, as the layout keeps them
+    # The oracle's padding entries are zero, as its layout keeps them; the
+    # GPU state gets the same buffers with non-zero padding.  A step ignores
+    # padding and stores it back as zero, so after it the two must agree
+    # everywhere (padding included).
     seg = 0
+    gpu_bufs = {}
     for n in numels:
         for name, buf in ost.buffers().items():
             if not name.endswith("scale"):
                 buf[seg + n:seg + oracle.pad16(n)] = 0
         seg += oracle.pad16(n)
-    st = ma.adam_state_create(numels, storage, amsgrad=ams)
     for name, buf in ost.buffers().items():
+        b = buf.copy()
+        if not name.endswith("scale"):
+            seg = 0
+            for n in numels:
+                pad = slice(seg + n, seg + oracle.pad16(n))
+                if name.endswith("bf16"):
+                    b[pad] = oracle.bf16_from_f32(np.full(b[pad].size, 0.5, np.float32))
+                elif name == "m_f32":
+                    b[pad] = np.float32(-0.5)
+                else:
+                    b[pad] = 127 if name == "m_codes" else 255
+                seg += oracle.pad16(n)
+        gpu_bufs[name] = b
+    st = ma.adam_state_create(numels, storage, amsgrad=ams)
+    for name, buf in gpu_bufs.items():
         src = torch.from_numpy(buf.view(np.int16) if name.endswith("bf16") else buf).cuda()
         ma.adam_state_write(st, name, src)
     params = workloads.host_params(22, numels)
@@ -1054,3 +1072,109 @@ def test_checkpoint_rejects_a_corrupted_stream():
     st.destroy()
     empty.destroy()
     again.destroy()
+
+
+# ---------------------------------------------------------------- exact rounding ties
+# Nearest rounding breaks ties to even (reading S8; the 8-bit Adam page names
+# only the stochastic option).  With beta1 = beta2 = 0 the new moments are
+# m = g and v = fl(g*g) exactly, so gradients can be placed on exact ties:
+#   first moment: block maximum 127 * 2^-12 gives r = fl(127 / A) = 2^12, and
+#     |g| = (k + 1/2) * 2^-12 gives y = k + 1/2 exactly;
+#   second moment: for a block maximum g_max (A = fl(g_max^2), r = fl(255/A)),
+#     a host search finds fp32 g with fl(fl(g*g) * r) = k + 1/2 exactly (six
+#     block scales between them reach 247 of the 255 half-integers).
+# Codes must then match the oracle bit for bit (not within +-1), and the tie
+# codes must be the even neighbours.
+_TIE_GMAX = [2.0 ** -10 * f for f in (1.0, 1.5, 1.25, 1.75, 1.125, 1.375)]
+
+
+def _v_tie_blocks():
+    """[(g_max, [(k, g), ...]) per block]: fp32 gradients whose squares land
+    on y = k + 1/2 in a block whose maximum gradient is g_max."""
+    cover = {}
+    blocks = []
+    for gm in _TIE_GMAX:
+        gm = np.float32(gm)
+        r = np.float32(255.0) / (gm * gm)
+        ties = []
+        for k in range(255):
+            if k in cover:
+                continue
+            yt = np.float32(k + 0.5)
+            g0 = np.float32(np.sqrt(float(yt) / float(r)))
+            cand = (g0.view(np.uint32).astype(np.int64) + np.arange(-64, 65)).astype(
+                np.uint32).view(np.float32)
+            hit = np.nonzero(((cand * cand) * r == yt) & (cand < gm))[0]
+            if hit.size:
+                cover[k] = True
+                ties.append((k, cand[hit[0]]))
+        blocks.append((gm, ties))
+    assert sum(len(t) for _, t in blocks) >= 240
+    return blocks
+
+
+def _tie_inputs():
+    """Two tensors: m ties (3 blocks, the last ragged) and v ties (one block
+    per block scale, the last ragged).  Returns grads, and per tensor the
+    expected (index, code) of every tie element for m and for v."""
+    rng = np.random.default_rng(77)
+    # first-moment ties
+    n0 = 2 * 2048 + 700
+    k = rng.integers(0, 127, n0)
+    sgn = np.where(rng.random(n0) < 0.5, -1, 1)
+    g0 = (sgn * (k + 0.5) * 2.0 ** -12).astype(np.float32)
+    maxpos = [0, 2048, 4096]
+    for b, i in enumerate(maxpos):
+        g0[i] = np.float32((1 if b % 2 == 0 else -1) * 127 * 2.0 ** -12)
+    m_ties = [(i, int(sgn[i]) * int(k[i] + (k[i] & 1))) for i in range(n0) if i not in maxpos]
+    # second-moment ties
+    vblocks = _v_tie_blocks()
+    n1 = 2048 * (len(vblocks) - 1) + 1500
+    g1 = np.zeros(n1, np.float32)
+    v_ties = []
+    for b, (gm, ties) in enumerate(vblocks):
+        base = 2048 * b
+        length = min(2048, n1 - base)
+        g1[base] = gm
+        for j in range(1, length):
+            kk, g = ties[(j - 1) % len(ties)]
+            g1[base + j] = g if rng.random() < 0.5 else -g
+            v_ties.append((base + j, kk + (kk & 1)))
+    return [g0, g1], m_ties, v_ties
+
+
+@pytest.mark.parametrize("storage,ams,pct", [("q8", False, None), ("q8", True, None),
+                                             ("q8", False, 100.0), ("q8_v_only", False, None),
+                                             ("q8_v_only", True, 100.0)])
+def test_nearest_rounding_ties_to_even(storage, ams, pct):
+    grads, m_ties, v_ties = _tie_inputs()
+    numels = [g.size for g in grads]
+    hp = dict(lr=1e-3, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.01, percentile=pct)
+    params = workloads.host_params(31, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, storage, amsgrad=ams)
+    ost = oracle.OracleState(numels, storage, amsgrad=ams)
+    seg1 = oracle.pad16(numels[0])
+    stats = Stats()
+    for t in (1, 2):
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for i in range(2):
+            compare_params(dev_p[i].cpu().numpy(), params[i], stats, f"t={t} tensor {i}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            # bit-exact codes, not the +-1 allowance of nearest rounding
+            compare_buffer(nm, got[nm], want, True, stats, f"t={t}")
+        if storage == "q8":
+            mc = got["m_codes"].astype(np.int64)
+            idx = np.array([i for i, _ in m_ties])
+            assert np.array_equal(mc[idx], np.array([c for _, c in m_ties])), "m tie codes"
+        vidx = seg1 + np.array([i for i, _ in v_ties])
+        vwant = np.array([c for _, c in v_ties])
+        assert np.array_equal(got["v_codes"][vidx].astype(np.int64), vwant), "v tie codes"
+        if ams:  # the running maximum equals v here (w_old <= v at both steps)
+            assert np.array_equal(got["vmax_codes"][vidx].astype(np.int64), vwant)
+    log(f"ties to even, {storage} ams={ams} pct={pct}: {len(m_ties)} m and {len(v_ties)} v "
+        f"tie elements; {stats}")
+    st.destroy()

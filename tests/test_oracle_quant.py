@@ -176,3 +176,59 @@ def test_tiny_block_statistic_encodes_zero(orc):
     x = np.full(8, np.float32(2.0 ** -120), np.float32)
     codes, A = orc.quantize_block(x, True)
     assert A == 0 and not codes.any()
+
+
+# -------------------------------------------------------------- exact ties
+# Reading S8 (nearest rounding breaks ties to even; the 8-bit Adam page names
+# only the stochastic option, so deterministic ties are a reading): a block
+# whose statistic is A = qmax * 2^e has r = fl(qmax / A) = 2^-e exactly, so an
+# element of magnitude (k + 1/2) * 2^e lands on y = k + 1/2 with no rounding
+# at all, and its code must be the even one of k and k + 1.  A quantizer that
+# rounds half away from zero (or half up) differs on every odd k.
+@pytest.mark.parametrize("signed", [True, False])
+@pytest.mark.parametrize("e", [-100, -20, -3, 0, 7, 40])
+def test_nearest_rounding_ties_go_to_even(orc, signed, e):
+    qmax = 127 if signed else 255
+    scale = np.float32(2.0 ** e)
+    k = np.arange(qmax, dtype=np.int64)                  # 0 .. qmax-1
+    mags = (k.astype(np.float32) + np.float32(0.5)) * scale  # exact
+    want = np.where(k % 2 == 0, k, k + 1)                 # the even neighbour
+    if signed:
+        x = np.concatenate([mags, -mags, [np.float32(qmax) * scale]]).astype(np.float32)
+        want_codes = np.concatenate([want, -want, [qmax]])
+    else:
+        x = np.concatenate([mags, [np.float32(qmax) * scale]]).astype(np.float32)
+        want_codes = np.concatenate([want, [qmax]])
+    # the statistic found in the block (its maximum) and the one given
+    codes, A = orc.quantize_block(x, signed)
+    assert A == np.float32(qmax) * scale
+    assert np.array_equal(codes, want_codes)
+    codes2, _ = orc.quantize_with_stat(x, signed, float(np.float32(qmax) * scale))
+    assert np.array_equal(codes2, want_codes)
+    # the percentile statistic at 100 is the same maximum
+    codes3, _ = orc.quantize_block(x, signed, use_pct=True, p=100.0)
+    assert np.array_equal(codes3, want_codes)
+
+
+def test_step_ties_go_to_even(orc):
+    # A whole 8-bit step in which the moments land on exact ties: with
+    # beta1 = beta2 = 0 the new first moment is the gradient itself and the
+    # second moment its square, and the block layout below makes the first
+    # moment's y = |m| * fl(127/A) an exact half-integer on every element but
+    # the block maximum.
+    rng = np.random.default_rng(41)
+    n = 2048 + 700
+    k = rng.integers(0, 127, n)
+    sign = np.where(rng.random(n) < 0.5, -1.0, 1.0)
+    g = (sign * (k + 0.5) * 2.0 ** -12).astype(np.float32)
+    g[0] = np.float32(127 * 2.0 ** -12)       # block 0's maximum
+    g[2048] = np.float32(-127 * 2.0 ** -12)   # block 1's maximum (ragged block)
+    st = orc.OracleState([n], "q8")
+    p = [np.zeros(n, np.float32)]
+    st.step(p, [g], lr=1e-3, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.0, t=1,
+            decoupled=True, stochastic=False, percentile=None, seed=1)
+    codes = st.buffers()["m_codes"][:n].astype(np.int64)
+    want = np.where(k % 2 == 0, k, k + 1) * sign.astype(np.int64)
+    want[0], want[2048] = 127, -127
+    assert np.array_equal(codes, want)
+    assert np.array_equal(st.buffers()["m_scale"], np.float32([127 * 2.0 ** -12] * 2))
