@@ -117,7 +117,8 @@ enum adam_buffer {
     ADAM_BUF_M_F32 = 6,   /* float[padded elements]    (Q8_V_ONLY) */
     ADAM_BUF_VMAX_CODES = 7, /* uint8[padded elements] (Q8, Q8_V_ONLY with AMSGRAD) */
     ADAM_BUF_VMAX_SCALE = 8, /* float[blocks]          (Q8, Q8_V_ONLY with AMSGRAD) */
-    ADAM_BUF_VMAX_BF16 = 9   /* uint16[padded elements] (BF16 with AMSGRAD) */
+    ADAM_BUF_VMAX_BF16 = 9,  /* uint16[padded elements] (BF16 with AMSGRAD) */
+    ADAM_BUF_COUNT = 10      /* number of buffer ids */
 };
 
 enum adam_options {
@@ -274,6 +275,43 @@ int32_t adam_state_describe(const adam_state *s, adam_layout *layout, int64_t *n
 /* Frees every buffer of the state (after synchronizing the device).
    NULL is ignored. */
 void adam_state_destroy(adam_state *s);
+
+/*
+ * adam_step_noalloc -- for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same step as adam_step (same kernels, same results bit for
+ * bit) over state buffers the caller owns, with no state object, no
+ * allocation and no host-to-device copy: the block-descriptor, pointer and
+ * draw-index tables that adam_state_create would allocate live in one fixed
+ * device array of the library (17.5 MiB per GPU, held until the process
+ * ends) and are written by small fill kernels from kernel arguments, on
+ * hip_stream, before the step kernel.
+ *   numels, layout: the tensor list and layout, as for adam_state_create.
+ *   params, grads: as for adam_step.
+ *   state: ADAM_BUF_COUNT device pointers indexed by enum adam_buffer; the
+ *     entries of the buffers the layout has (see adam_state_read) must point
+ *     at caller-owned device memory of exactly the sizes a state of this
+ *     tensor list would have (padded elements = sum of pad16(numel); blocks =
+ *     sum of ceil(numel / 2048); scales in tensor-major block order), each
+ *     16-byte aligned; the others are ignored.  A new state is all zeros.
+ *   draw_index: per tensor, the stochastic-rounding draw index of element 0
+ *     (see adam_state_set_draw_index), or NULL for the flat index.
+ * Limits: at most 65536 tensors and 2^20 blocks (2^31 elements) per call;
+ * larger lists return EINVAL with a message naming the limit.
+ * Every call on a GPU shares that GPU's table array, and a call's tables
+ * stay there until the next call rewrites them: calls that overlap on one
+ * GPU (two streams, or two host threads, without ordering between them)
+ * race on the tables and must not be issued.  Calls ordered on one stream
+ * are safe.  A graph capture records the fill kernels with the step, so a
+ * replay rewrites its own tables; it repeats the call as recorded (same t,
+ * hyperparameters and pointers).
+ * Errors (no work enqueued): EINVAL (as adam_state_bytes and adam_step, a
+ * NULL state array or needed buffer, the limits above), EALIGN; EDEVICE if
+ * a launch fails.
+ */
+int adam_step_noalloc(int32_t n_tensors, const int64_t *numels, const adam_layout *layout,
+                      float *const *params, const void *const *grads, void *const *state,
+                      const int64_t *draw_index, const adam_hparams *hp, void *hip_stream);
 
 /* Thread-local description of the last error on this thread ("" if none). */
 const char *adam_last_error(void);

@@ -29,6 +29,8 @@ from ._binding import (  # noqa: F401
     adam_state_set_draw_index,
     adam_state_write,
     adam_step,
+    adam_step_noalloc,
     library,
     library_path,
+    state_buffer_sizes,
 )

@@ -78,6 +78,9 @@ def library():
     L.adam_state_set_draw_index.restype = ctypes.c_int
     L.adam_state_get_draw_index.argtypes = [vp, i64p, ctypes.c_int32]
     L.adam_state_get_draw_index.restype = ctypes.c_int32
+    L.adam_step_noalloc.argtypes = [ctypes.c_int32, i64p, ctypes.POINTER(adam_layout), vp, vp, vp,
+                                    i64p, ctypes.POINTER(adam_hparams), vp]
+    L.adam_step_noalloc.restype = ctypes.c_int
     L.adam_state_destroy.argtypes = [vp]
     L.adam_state_destroy.restype = None
     L.adam_last_error.argtypes = []
@@ -236,6 +239,61 @@ def _hparams(lr, beta1, beta2, eps, weight_decay, t, decoupled, stochastic, perc
              | (_F_STATIC_SCALES if static_scales else 0))
     return adam_hparams(lr, beta1, beta2, eps, weight_decay,
                         100.0 if percentile is None else percentile, int(t), flags, 0, int(seed))
+
+
+def state_buffer_sizes(numels, storage, amsgrad=False):
+    """{buffer name: bytes} of every state buffer a layout has, for caller-owned
+    state (adam_step_noalloc): padded elements = sum of pad16(numel), blocks =
+    sum of ceil(numel / 2048), as include/adam_mi355x.h lays them out."""
+    padded = sum((int(n) + 15) // 16 * 16 for n in numels)
+    blocks = sum(-(-int(n) // ADAM_BLOCK_SIZE) for n in numels)
+    sizes = {"bf16": {"m_bf16": 2 * padded, "v_bf16": 2 * padded},
+             "q8": {"m_codes": padded, "v_codes": padded, "m_scale": 4 * blocks,
+                    "v_scale": 4 * blocks},
+             "q8_v_only": {"v_codes": padded, "v_scale": 4 * blocks, "m_f32": 4 * padded}}[storage]
+    if amsgrad:
+        sizes.update({"vmax_bf16": 2 * padded} if storage == "bf16"
+                     else {"vmax_codes": padded, "vmax_scale": 4 * blocks})
+    return sizes
+
+
+def adam_step_noalloc(params, grads, buffers, *, storage, grad_dtype="f32", amsgrad=False, lr,
+                      beta1, beta2, eps, weight_decay, t, decoupled=True, stochastic=False,
+                      percentile=None, seed=42, static_scales=False, draw_index=None,
+                      stream=None):
+    """The allocation-free step over caller-owned state: buffers maps each
+    buffer name of the layout (state_buffer_sizes) to a contiguous device
+    tensor of exactly that many bytes (zeros for a new state).  The library
+    allocates nothing; its tables live in a fixed device array (calls that
+    overlap on one GPU race on it)."""
+    numels = [int(p.numel()) for p in params]
+    lay = _layout(storage, grad_dtype, ADAM_BLOCK_SIZE, OPT_AMSGRAD if amsgrad else 0)
+    _check_step_tensors(AdamState(None, numels, lay), params, grads)
+    want = state_buffer_sizes(numels, storage, amsgrad)
+    if set(buffers) != set(want):
+        raise ValueError(f"buffers must be exactly {sorted(want)}, got {sorted(buffers)}")
+    S = (ctypes.c_void_p * len(BUFFERS))()
+    for name, nbytes in want.items():
+        b = buffers[name]
+        if b.numel() * b.element_size() != nbytes or not b.is_contiguous():
+            raise ValueError(f"buffer {name}: must be a contiguous tensor of {nbytes} bytes")
+        if nbytes and not b.is_cuda:
+            raise ValueError(f"buffer {name}: must be a device tensor")
+        S[BUFFERS[name]] = b.data_ptr()
+    n, arr = _numels(numels)
+    P = (ctypes.c_void_p * max(n, 1))(*[p.data_ptr() for p in params])
+    G = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
+    D = None
+    if draw_index is not None:
+        if len(draw_index) != n:
+            raise ValueError(f"expected {n} draw indices")
+        D = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in draw_index])
+    hp = _hparams(lr, beta1, beta2, eps, weight_decay, t, decoupled, stochastic, percentile, seed,
+                  static_scales)
+    _check(library().adam_step_noalloc(n, arr, ctypes.byref(lay), ctypes.cast(P, ctypes.c_void_p),
+                                       ctypes.cast(G, ctypes.c_void_p),
+                                       ctypes.cast(S, ctypes.c_void_p), D, ctypes.byref(hp),
+                                       _stream(stream)))
 
 
 def adam_state_buffer_bytes(state, which):

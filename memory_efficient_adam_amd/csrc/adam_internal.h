@@ -71,4 +71,44 @@ struct Variant {
 // Enqueues the step kernel over every descriptor.
 hipError_t launch_step(const Variant &v, const StepArgs &a, hipStream_t stream);
 
+// ---------------------------------------------------------------- allocation-free step
+// The allocation-free entry point keeps the tables a state would own (block
+// descriptors, per-tensor pointer pairs and draw indices) in one file-scope
+// device array of the kernel module, so it allocates nothing.  Its limits:
+constexpr uint32_t kScratchMaxTensors = 65536;
+constexpr uint32_t kScratchMaxBlocks = 1u << 20;  // 2^31 elements in 2048-blocks
+
+// The device address of the scratch tables on `device` (which must be the
+// current device): taken once per device with hipGetSymbolAddress, then
+// cached.  desc[kScratchMaxBlocks], tensors[kScratchMaxTensors],
+// draw[kScratchMaxTensors].
+hipError_t scratch_tables(int device, BlockDesc **desc, TensorRef **tensors, uint64_t **draw);
+
+// One tensor's entries of the scratch tables, written on the device by a
+// fill kernel (48 bytes, passed in the kernel arguments).
+struct FillTensor {
+    float *p;
+    const void *g;
+    uint64_t draw;        // draw index of element 0
+    uint32_t n;           // numel (>= 1)
+    uint32_t gidx16;      // flat index of element 0 / 16
+    uint32_t first_full;  // descriptor index of its first full block
+    uint32_t tail;        // descriptor index of its ragged last block (if n % 2048)
+    uint32_t first_slot;  // scale slot of its first block
+    uint32_t index;       // tensor index
+};
+static_assert(sizeof(FillTensor) == 48, "fill entry layout");
+
+constexpr int kFillChunk = 64;  // tensors per fill launch (kernel arguments < 4 KiB)
+struct FillArgs {
+    BlockDesc *desc;
+    TensorRef *tensors;
+    uint64_t *draw;
+    uint32_t count;  // entries of t[] used
+    uint32_t pad;
+    FillTensor t[kFillChunk];
+};
+
+hipError_t launch_fill(const FillArgs &f, hipStream_t stream);
+
 }  // namespace adam_mi355x

@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "adam_internal.h"
 
@@ -1096,10 +1097,66 @@ hipError_t launch_storage(const Variant &v, const StepArgs &a, hipStream_t strea
     }
 }
 
+// ---------------------------------------------------------------- allocation-free step tables
+// The tables of the allocation-free entry point: block descriptors, then
+// per-tensor pointer pairs, then per-tensor draw indices.  One copy per GPU,
+// held until the process ends (17.5 MiB); every call on a GPU rewrites the
+// parts it uses before its step kernel reads them.
+constexpr size_t kScratchDescBytes = (size_t)kScratchMaxBlocks * sizeof(BlockDesc);
+constexpr size_t kScratchTensorBytes = (size_t)kScratchMaxTensors * sizeof(TensorRef);
+constexpr size_t kScratchBytes = kScratchDescBytes + kScratchTensorBytes + (size_t)kScratchMaxTensors * 8;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// One workgroup row per tensor of the chunk (blockIdx.x), the tensor's blocks
+// spread over blockIdx.y and the threads.  Ordinary vector stores.
+__global__ void __launch_bounds__(kThreads) fill_tables_kernel(FillArgs f) {
+    const FillTensor &t = f.t[blockIdx.x];
+    const uint32_t nblk = (t.n + kBlock - 1) / kBlock, full = t.n / kBlock;
+    for (uint32_t b = blockIdx.y * kThreads + threadIdx.x; b < nblk; b += gridDim.y * kThreads) {
+        const uint32_t len = b < full ? (uint32_t)kBlock : t.n - full * kBlock;
+        f.desc[b < full ? t.first_full + b : t.tail] =
+            BlockDesc{t.gidx16 + b * (kBlock / 16), t.index, (b << kBlockBits) | (len - 1u), t.first_slot + b};
+    }
+    if (blockIdx.y == 0 && threadIdx.x == 0) {
+        f.tensors[t.index] = TensorRef{t.p, t.g};
+        f.draw[t.index] = t.draw;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_step(const Variant &v, const StepArgs &a, hipStream_t stream) {
     return v.amsgrad ? launch_storage<true>(v, a, stream) : launch_storage<false>(v, a, stream);
+}
+
+hipError_t scratch_tables(int device, BlockDesc **desc, TensorRef **tensors, uint64_t **draw) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *base[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!base[device]) {
+        // the array's name is a host-side stand-in: its device address on the
+        // current device comes from the runtime, once per device
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        base[device] = p;
+    }
+    unsigned char *b = static_cast<unsigned char *>(base[device]);
+    *desc = reinterpret_cast<BlockDesc *>(b);
+    *tensors = reinterpret_cast<TensorRef *>(b + kScratchDescBytes);
+    *draw = reinterpret_cast<uint64_t *>(b + kScratchDescBytes + kScratchTensorBytes);
+    return hipSuccess;
+}
+
+hipError_t launch_fill(const FillArgs &f, hipStream_t stream) {
+    if (f.count == 0 || f.count > (uint32_t)kFillChunk) return hipErrorInvalidValue;
+    uint32_t most = 1;
+    for (uint32_t k = 0; k < f.count; ++k) most = std::max(most, (f.t[k].n + kBlock - 1) / kBlock);
+    const uint32_t rows = std::min<uint32_t>((most + kThreads - 1) / kThreads, 256u);
+    hipLaunchKernelGGL(fill_tables_kernel, dim3(f.count, rows), dim3(kThreads), 0, stream, f);
+    return hipGetLastError();
 }
 
 }  // namespace adam_mi355x

@@ -767,3 +767,112 @@ int adam_step(adam_state *s, float *const *params, const void *const *grads, con
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free step
+
+extern "C" {
+
+int adam_step_noalloc(int32_t n_tensors, const int64_t *numels, const adam_layout *layout, float *const *params,
+                      const void *const *grads, void *const *state, const int64_t *draw_index,
+                      const adam_hparams *hp, void *hip_stream) {
+    return guarded([&]() -> int {
+        int rc = check_numels(n_tensors, numels);
+        if (rc) return rc;
+        if ((rc = check_layout(layout))) return rc;
+        if ((rc = check_hparams(hp, layout->storage))) return rc;
+        if (n_tensors > (int32_t)kScratchMaxTensors)
+            return fail(ADAM_EINVAL, "adam_step_noalloc takes at most " + std::to_string(kScratchMaxTensors) +
+                                         " tensors, got " + std::to_string(n_tensors));
+        int64_t nblocks = 0, padded = 0;
+        for (int32_t k = 0; k < n_tensors; ++k) {
+            nblocks += blocks_of(numels[k]);
+            padded += pad16(numels[k]);
+        }
+        if (nblocks > (int64_t)kScratchMaxBlocks)
+            return fail(ADAM_EINVAL, "adam_step_noalloc takes at most " + std::to_string(kScratchMaxBlocks) +
+                                         " blocks of 2048 elements (its fixed table space), got " +
+                                         std::to_string(nblocks));
+        if (n_tensors > 0 && (!params || !grads)) return fail(ADAM_EINVAL, "params or grads is NULL");
+        for (int32_t k = 0; k < n_tensors; ++k) {
+            if (numels[k] == 0) continue;
+            if (!params[k] || !grads[k]) return fail(ADAM_EINVAL, "NULL pointer for tensor " + std::to_string(k));
+            if ((reinterpret_cast<uintptr_t>(params[k]) | reinterpret_cast<uintptr_t>(grads[k])) & 15u)
+                return fail(ADAM_EALIGN, "tensor " + std::to_string(k) + " is not 16-byte aligned");
+        }
+        if (!state) return fail(ADAM_EINVAL, "state buffer array is NULL");
+        for (int32_t b : buffers_of(*layout)) {
+            if (padded == 0) break;
+            if (!state[b]) return fail(ADAM_EINVAL, "state buffer " + std::to_string(b) + " is NULL");
+            if (reinterpret_cast<uintptr_t>(state[b]) & 15u)
+                return fail(ADAM_EALIGN, "state buffer " + std::to_string(b) + " is not 16-byte aligned");
+        }
+        if (draw_index && (rc = check_draw_first(n_tensors, numels, draw_index))) return rc;
+        if (nblocks == 0) return ADAM_OK;
+
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        BlockDesc *desc = nullptr;
+        TensorRef *tensors = nullptr;
+        uint64_t *draw = nullptr;
+        if ((e = scratch_tables(dev, &desc, &tensors, &draw)) != hipSuccess)
+            return hip_fail(e, "scratch table address (hipGetSymbolAddress)");
+        hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+
+        // the tables, written on the device from kernel arguments (no host
+        // staging buffer, no copy): full blocks first, then the ragged ones
+        int64_t n_full = 0;
+        for (int32_t k = 0; k < n_tensors; ++k) n_full += numels[k] / kBlock;
+        FillArgs f{};
+        f.desc = desc;
+        f.tensors = tensors;
+        f.draw = draw;
+        int64_t full_at = 0, tail_at = n_full, slot = 0, seg = 0;
+        for (int32_t k = 0; k < n_tensors; ++k) {
+            const int64_t n = numels[k];
+            if (n > 0) {
+                FillTensor &t = f.t[f.count++];
+                t.p = params[k];
+                t.g = grads[k];
+                t.draw = draw_index ? (uint64_t)draw_index[k] : (uint64_t)seg;
+                t.n = (uint32_t)n;
+                t.gidx16 = (uint32_t)(seg / 16);
+                t.first_full = (uint32_t)full_at;
+                t.tail = (uint32_t)tail_at;
+                t.first_slot = (uint32_t)slot;
+                t.index = (uint32_t)k;
+                if (f.count == (uint32_t)kFillChunk) {
+                    if ((e = launch_fill(f, stream)) != hipSuccess) return hip_fail(e, "table fill launch");
+                    f.count = 0;
+                }
+            }
+            full_at += n / kBlock;
+            tail_at += (n % kBlock) != 0;
+            slot += blocks_of(n);
+            seg += pad16(n);
+        }
+        if (f.count > 0 && (e = launch_fill(f, stream)) != hipSuccess) return hip_fail(e, "table fill launch");
+
+        StepArgs a{};
+        a.desc = desc;
+        a.tensors = tensors;
+        a.draw_first = draw;
+        const int32_t st = layout->storage;
+        const bool ams = amsgrad(*layout);
+        a.m_state = state[st == ADAM_STORE_BF16 ? ADAM_BUF_M_BF16 : (st == ADAM_STORE_Q8 ? ADAM_BUF_M_CODES : ADAM_BUF_M_F32)];
+        a.v_state = state[st == ADAM_STORE_BF16 ? ADAM_BUF_V_BF16 : ADAM_BUF_V_CODES];
+        a.m_scale = st == ADAM_STORE_Q8 ? static_cast<float *>(state[ADAM_BUF_M_SCALE]) : nullptr;
+        a.v_scale = st != ADAM_STORE_BF16 ? static_cast<float *>(state[ADAM_BUF_V_SCALE]) : nullptr;
+        a.w_state = ams ? state[st == ADAM_STORE_BF16 ? ADAM_BUF_VMAX_BF16 : ADAM_BUF_VMAX_CODES] : nullptr;
+        a.w_scale = ams && st != ADAM_STORE_BF16 ? static_cast<float *>(state[ADAM_BUF_VMAX_SCALE]) : nullptr;
+        fill_scalars(a, hp);
+        a.n_full = (uint32_t)n_full;
+        a.n_all = (uint32_t)nblocks;
+        Variant v{st, layout->grad_dtype == ADAM_GRAD_BF16, (hp->flags & ADAM_F_STOCHASTIC) != 0,
+                  (hp->flags & ADAM_F_PERCENTILE) != 0, (hp->flags & ADAM_F_STATIC_SCALES) != 0, ams};
+        if ((e = launch_step(v, a, stream)) != hipSuccess) return hip_fail(e, "kernel launch");
+        return ADAM_OK;
+    });
+}
+
+}  // extern "C"

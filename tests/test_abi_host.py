@@ -300,3 +300,20 @@ def test_state_read_write_reject_wrong_sizes():
     finally:
         B.adam_state_buffer_bytes = orig
 
+
+def test_noalloc_limits_refused_before_any_device_call():
+    # the allocation-free step's table space is fixed: 65536 tensors and 2^20
+    # blocks; larger lists are refused with a message naming the limit, before
+    # any HIP call (the pointers below are never dereferenced)
+    lib = ma.library()
+    lay = B.adam_layout(2, 0, 2048, 0)
+    hp = B.adam_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 100.0, 1, 1, 0, 42)
+    for numels, what in (([0] * 70000, b"65536"), ([2 ** 31 + 1], b"1048576")):
+        n = len(numels)
+        arr = (ctypes.c_int64 * n)(*numels)
+        ptrs = (ctypes.c_void_p * n)(*([4096] * n))
+        state = (ctypes.c_void_p * 10)(*([4096] * 10))
+        rc = lib.adam_step_noalloc(n, arr, ctypes.byref(lay), ctypes.cast(ptrs, ctypes.c_void_p),
+                                   ctypes.cast(ptrs, ctypes.c_void_p),
+                                   ctypes.cast(state, ctypes.c_void_p), None, ctypes.byref(hp), None)
+        assert rc == -1 and what in lib.adam_last_error(), lib.adam_last_error()
