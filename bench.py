@@ -3,15 +3,21 @@
 A step is one adam_step call through the C ABI -- one kernel launch over
 every tensor of the set (dequantize / bias-corrected update / block
 statistic / requantize, or the bf16-moment variant) -- on synthetic inputs
-already resident in HBM.  Default workload: the ViT-Base shaped set (152
-tensors, 86,567,656 fp32 params, fp32 grads ~N(0, 1e-3)) with bf16 moments.
-Other sets: --config (see workloads.CONFIGS).
+already resident in HBM.  Headline workload (`value`): the ViT-Base shaped
+set (152 tensors, 86,567,656 fp32 params, fp32 grads ~N(0, 1e-3)) with bf16
+moments.  With no --config the same JSON line also carries `modes`: the
+8-bit sets timed the same way -- ViT-Base with 8-bit m and v, the GPT-1.3B
+shaped set with Philox stochastic rounding and bf16 grads, the Llama-7B
+shaped set with fp32 m, 8-bit v and the 99.9th-percentile scale.  Other sets:
+--config (see workloads.CONFIGS).
 
-Prints one JSON line: Gparams/s, the roofline of the step kernel
-(algorithmic bytes per launch / average launch time from HIP events on the
-launch stream, against the 8 TB/s HBM peak; HBM traffic from rocprofv3
-FETCH_SIZE / WRITE_SIZE counters when a committed counter summary matches
-the current kernel source) and the CPU oracle timed on a bounded sample.
+Each record: Gparams/s, the roofline of the step kernel (algorithmic bytes
+per launch / average launch time from HIP events on the launch stream,
+against the 8 TB/s HBM peak; HBM traffic from rocprofv3 FETCH_SIZE /
+WRITE_SIZE counters when a committed counter summary matches the current
+kernel source) and the CPU oracle timed on the same workload recipe, once on
+one thread and once on all the host cores it may use (threads over disjoint
+block ranges of the oracle's sampled-block entry point).
 """
 import argparse
 import dataclasses
@@ -80,31 +86,187 @@ def traffic_for(workload):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(cfg, hp, min_seconds=10.0, max_steps=20):
-    """The oracle, as it is, on whole steps of the same workload (single
-    thread), same recipe of inputs generated on the host: steps are run
-    until at least min_seconds of oracle time (input generation untimed)."""
-    import numpy as np  # noqa: F401
+def _block_list(numels, block=2048):
+    """(length, flat index) of every block of a tensor list, tensor-major,
+    tensors padded to 16 elements in the flat state (layout only)."""
+    out, seg = [], 0
+    for n in numels:
+        for s0 in range(0, n, block):
+            out.append((min(block, n - s0), seg + s0))
+        seg += (n + 15) // 16 * 16
+    return out
+
+
+def host_threads():
+    """Host cores the oracle may use: the process's CPU affinity, capped by
+    OMP_NUM_THREADS when set (the GPU machine allots a share of its cores)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(cfg, hp, max_blocks=None, min_seconds=8.0, max_steps=12):
+    """The oracle, as it is, on the same workload recipe (host-generated
+    inputs of the set's value laws; generation not timed): whole steps over
+    every block of the set, or over a seeded sample of max_blocks blocks.
+    Timed twice on the same inputs: single-threaded, and with the blocks
+    split into contiguous ranges stepped concurrently by a thread pool (the
+    oracle's C entry point runs without the interpreter lock).  Steps are
+    repeated until min_seconds of single-threaded oracle time."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     import workloads
+    blocks = _block_list(cfg.numels())
+    label = f"every block of the {cfg.name} set"
+    if max_blocks is not None and len(blocks) > max_blocks:
+        rng = np.random.default_rng([cfg.cfg_id, 7])
+        pick = np.sort(rng.choice(len(blocks), max_blocks, replace=False))
+        blocks = [blocks[i] for i in pick]
+        label = f"a seeded sample of {max_blocks} of the {cfg.name} set's blocks"
+    lens = [n for n, _ in blocks]
+    n_params = sum(lens)
+    grad_bf16 = cfg.grad_dtype == "bf16"
+    threads = host_threads()
+    bounds = [len(blocks) * k // threads for k in range(threads + 1)]
+    ranges = [(bounds[k], bounds[k + 1]) for k in range(threads) if bounds[k + 1] > bounds[k]]
+
+    def run(n_workers, steps_cap, seconds):
+        """(Gparams/s, steps): steps t = 1, 2, ... over the same inputs until
+        `seconds` of oracle time or `steps_cap` steps."""
+        params = workloads.host_params(cfg.cfg_id, lens)
+        parts = [oracle.OracleBlocks(blocks[a:b], cfg.storage, grad_bf16=grad_bf16,
+                                     amsgrad=cfg.amsgrad) for a, b in ranges]
+        elapsed, steps = 0.0, 0
+        with ThreadPoolExecutor(max_workers=n_workers) as pool:
+            while steps < steps_cap and elapsed < seconds:
+                steps += 1
+                grads = workloads.host_grads(cfg.cfg_id, lens, steps, dist=cfg.grad_dist,
+                                             dtype=cfg.grad_dtype)
+                t0 = time.perf_counter()
+                futs = [pool.submit(part.step, params[a:b], grads[a:b], t=steps, **hp)
+                        for part, (a, b) in zip(parts, ranges)]
+                for f in futs:
+                    f.result()
+                elapsed += time.perf_counter() - t0
+        return n_params * steps / elapsed / 1e9, steps
+
+    one, steps = run(1, max_steps, min_seconds)
+    many, _ = run(threads, steps, float("inf"))  # the same steps on every core
+    return {"value": round(many, 5), "unit": "Gparams/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} step(s) over {label} ({n_params} params), the blocks split "
+                      f"into {len(ranges)} contiguous ranges stepped by {threads} threads; "
+                      "host-generated inputs of the workload's recipe, generation not timed",
+            "single_thread": {"value": round(one, 5), "unit": "Gparams/s", "cores": 1}}
+
+
+def apply_overrides(cfg, args):
+    """The workload's hyperparameters with the command line's overrides."""
+    hp = dict(cfg.hp)
+    if args.static_scales:
+        if cfg.storage == "bf16":
+            sys.exit("bench.py: --static-scales applies to 8-bit storage only")
+        hp["static_scales"] = True
+    if args.nearest:
+        if cfg.storage == "bf16":
+            sys.exit("bench.py: --nearest applies to 8-bit storage only")
+        hp["stochastic"] = False
+    if args.percentile is not None:
+        if cfg.storage == "bf16":
+            sys.exit("bench.py: --percentile applies to 8-bit storage only")
+        hp["percentile"] = args.percentile
+    return hp
+
+
+def time_workload(cfg, hp, steps, warmup, grad_buffers, traffic_key=None):
+    """Times `steps` back-to-back steps of one workload (after `warmup`
+    untimed ones) with HIP events on the launch stream; inputs resident in
+    HBM before the timed region.  Frees everything it allocated."""
+    import torch
+    import memory_efficient_adam_amd as ma
+    import workloads
     numels = cfg.numels()
-    params = workloads.host_params(cfg.cfg_id, numels)
-    st = oracle.OracleState(numels, cfg.storage, grad_bf16=(cfg.grad_dtype == "bf16"),
-                            amsgrad=cfg.amsgrad)
-    elapsed = 0.0
-    steps = 0
-    while elapsed < min_seconds and steps < max_steps:
-        steps += 1
-        grads = workloads.host_grads(cfg.cfg_id, numels, steps, dist=cfg.grad_dist,
-                                     dtype=cfg.grad_dtype)
-        t0 = time.perf_counter()
-        st.step(params, grads, t=steps, **hp)
-        elapsed += time.perf_counter() - t0
-    n = sum(numels)
-    return {"value": round(n * steps / elapsed / 1e9, 5), "unit": "Gparams/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{steps} full step(s) of the {cfg.name} workload ({n} params), "
-                      "single-threaded, host-generated inputs; generation not timed"}
+    n_params = sum(numels)
+    params = workloads.device_params(cfg.cfg_id, numels)
+    gsets = []
+    for i in range(max(1, grad_buffers)):
+        gsets.append(workloads.device_grads(cfg.cfg_id, numels, i + 1, dist=cfg.grad_dist,
+                                            dtype=cfg.grad_dtype))
+    st = ma.adam_state_create(numels, cfg.storage, cfg.grad_dtype, amsgrad=cfg.amsgrad)
+    stream = torch.cuda.current_stream()
+    t = 0
+    for _ in range(warmup):
+        t += 1
+        ma.adam_step(st, params, gsets[t % len(gsets)], t=t, stream=stream, **hp)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    # one event before each step and one after the last, all on the launch
+    # stream: per-step times as well as the whole timed region
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    start.record(stream)
+    marks[0].record(stream)
+    for k in range(steps):
+        t += 1
+        ma.adam_step(st, params, gsets[t % len(gsets)], t=t, stream=stream, **hp)
+        marks[k + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = start.elapsed_time(end) / steps
+    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(steps))
+    st.destroy()
+    del params, gsets
+    torch.cuda.empty_cache()
+
+    sec = ms / 1e3
+    alg = algorithmic_bytes(cfg)
+    achieved = alg / sec / 1e9
+    traffic = traffic_for(traffic_key) if traffic_key else None
+    return {
+        "value": round(n_params / sec / 1e9, 3),
+        "unit": "Gparams/s",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "wall_ms_per_step": round(wall * 1e3 / steps, 5),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 5),
+        "ms_per_step_min": round(per_step[0], 5),
+        "config": {
+            "workload": cfg.name,
+            "params": n_params,
+            "tensors": len(numels),
+            "blocks": sum(-(-k // 2048) for k in numels),
+            "storage": cfg.storage,
+            "grad_dtype": cfg.grad_dtype,
+            "stochastic_rounding": bool(hp.get("stochastic")),
+            "percentile": hp.get("percentile"),
+            "static_scales": bool(hp.get("static_scales")),
+            "amsgrad": cfg.amsgrad,
+            "block_size": 2048,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "traffic_source": (None if traffic is None else
+                               "profiles/hbm_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                               "of this kernel source on this workload, copy-calibrated"),
+            "algorithmic_bytes_per_launch": alg,
+        },
+    }
+
+
+# the 8-bit workloads timed beside the headline (bf16-moment) workload, with
+# the host-oracle sample size for each (blocks) and the grad buffers rotated
+MODES = [("vit_q8", 4096, 4), ("gpt1p3b_q8_sr", 4096, 4), ("llama7b_mf32_vq8_pct", 4096, 2)]
+TARGET_FRAC = 0.75
 
 
 def main():
@@ -112,7 +274,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="vit_bf16")
+    ap.add_argument("--config", default=None,
+                    help="one workload of workloads.CONFIGS (default: the ViT-Base bf16-moment "
+                         "headline plus the 8-bit modes)")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="headline workload only (skip the 8-bit mode records)")
     ap.add_argument("--grad-buffers", type=int, default=4,
                     help="distinct pre-generated gradient sets used in rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,7 +300,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import memory_efficient_adam_amd as ma
     import workloads
 
     torch.cuda.set_device(0)
@@ -148,108 +313,50 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}), flush=True)
         return
 
-    cfg = workloads.CONFIGS[args.config]
+    headline = args.config is None
+    cfg = workloads.CONFIGS[args.config or "vit_bf16"]
     if args.amsgrad:
         cfg = dataclasses.replace(cfg, amsgrad=True)
-    numels = cfg.numels()
-    n_params = sum(numels)
-    params = workloads.device_params(cfg.cfg_id, numels)
-    gsets = []
-    for i in range(max(1, args.grad_buffers)):
-        gsets.append(workloads.device_grads(cfg.cfg_id, numels, i + 1, dist=cfg.grad_dist,
-                                            dtype=cfg.grad_dtype))
-    st = ma.adam_state_create(numels, cfg.storage, cfg.grad_dtype, amsgrad=cfg.amsgrad)
-    stream = torch.cuda.current_stream()
-    hp = dict(cfg.hp)
-    if args.static_scales:
-        if cfg.storage == "bf16":
-            sys.exit("bench.py: --static-scales applies to 8-bit storage only")
-        hp["static_scales"] = True
-    if args.nearest:
-        if cfg.storage == "bf16":
-            sys.exit("bench.py: --nearest applies to 8-bit storage only")
-        hp["stochastic"] = False
-    if args.percentile is not None:
-        if cfg.storage == "bf16":
-            sys.exit("bench.py: --percentile applies to 8-bit storage only")
-        hp["percentile"] = args.percentile
-
-    t = 0
-    for _ in range(args.warmup):
-        t += 1
-        ma.adam_step(st, params, gsets[t % len(gsets)], t=t, stream=stream, **hp)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    # one event before each step and one after the last, all on the launch
-    # stream: per-step times as well as the whole timed region
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    start.record(stream)
-    marks[0].record(stream)
-    for k in range(args.steps):
-        t += 1
-        ma.adam_step(st, params, gsets[t % len(gsets)], t=t, stream=stream, **hp)
-        marks[k + 1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = start.elapsed_time(end) / args.steps
-    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
-    sec = ms / 1e3
-
-    alg = algorithmic_bytes(cfg)
-    achieved = alg / sec / 1e9
+    hp = apply_overrides(cfg, args)
     # counter readings are taken per workload for its own kernel variant (a
     # percentile run of an 8-bit set has its own record when one was taken)
     variant_changed = args.static_scales or cfg.amsgrad
-    key = cfg.name + ("_nearest" if args.nearest else "") + (
+    key = None if variant_changed else cfg.name + ("_nearest" if args.nearest else "") + (
         "" if args.percentile is None else f"_percentile{args.percentile}")
-    traffic = None if variant_changed else traffic_for(key)
+    rec = time_workload(cfg, hp, args.steps, args.warmup, args.grad_buffers, key)
     out = {
         "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",
-        "value": round(n_params / sec / 1e9, 3),
+        "value": rec["value"],
         "unit": "Gparams/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
-        "ms_per_step_median": round(per_step[len(per_step) // 2], 5),
-        "ms_per_step_min": round(per_step[0], 5),
+        "ms_per_step": rec["ms_per_step"],
+        "wall_ms_per_step": rec["wall_ms_per_step"],
+        "ms_per_step_median": rec["ms_per_step_median"],
+        "ms_per_step_min": rec["ms_per_step_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": cfg.name,
-            "params": n_params,
-            "tensors": len(numels),
-            "blocks": sum(-(-k // 2048) for k in numels),
-            "storage": cfg.storage,
-            "grad_dtype": cfg.grad_dtype,
-            "stochastic_rounding": bool(hp.get("stochastic")),
-            "percentile": hp.get("percentile"),
-            "static_scales": bool(hp.get("static_scales")),
-            "amsgrad": cfg.amsgrad,
-            "block_size": 2048,
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": alg,
-        },
+        "config": rec["config"],
+        "roofline": rec["roofline"],
     }
-    st.destroy()
-    del params, gsets
-    torch.cuda.empty_cache()
+    modes = []
+    if headline and not args.no_modes:
+        for name, sample_blocks, nbuf in MODES:
+            mcfg = workloads.CONFIGS[name]
+            m = time_workload(mcfg, dict(mcfg.hp), args.steps, args.warmup, nbuf, name)
+            m["target_frac"] = TARGET_FRAC
+            m["meets_target"] = m["roofline"]["frac"] >= TARGET_FRAC
+            modes.append((m, mcfg, sample_blocks))
+        out["modes"] = [m for m, _, _ in modes]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, hp)
+        for m, mcfg, sample_blocks in modes:
+            m["cpu_baseline"] = cpu_baseline(mcfg, dict(mcfg.hp), max_blocks=sample_blocks,
+                                             min_seconds=3.0)
     print(json.dumps(out), flush=True)
 
 
