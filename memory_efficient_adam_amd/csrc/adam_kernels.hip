@@ -165,94 +165,172 @@ __device__ __forceinline__ void block_max(float (&x)[N], float (*red)[kWaves]) {
     }
 }
 
-// rank-th smallest (0-based) of the block's 2048 keys (8 per thread) of each
-// of N moments at once: LDS radix select over the 31 magnitude bits in digits
-// of 11, 11 and 9 bits, one histogram per moment, so that the N selects share
-// each pass's four barriers.  Keys are |x| as bit patterns (the order of
-// non-negative floats); act[k] (block-uniform) skips moment k's work.
-template <int N>
-__device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N], uint32_t rank0,
-                               uint32_t (&out)[N], uint32_t (*hist)[kBlock], uint32_t (*scratch)[kWaves + 2]) {
+// One counting pass of the block select over N moments at once (one
+// histogram each, so the moments share the pass's four barriers): counts
+// digit(k, key) over the keys of moment k with take(k, key), then finds the
+// bin holding the rank[k]-th smallest of them; bin[k] and rank[k] (now the
+// rank within that bin) come back block-uniform.  act[k] (block-uniform)
+// skips moment k.  Keys are |x| as bit patterns (the order of non-negative
+// floats).
+template <int N, int kBins, class Digit, class Take>
+__device__ __forceinline__ void select_pass(const float *const (&x)[N], const bool (&act)[N], Digit digit,
+                                            Take take, uint32_t (&bin)[N], uint32_t (&rank)[N],
+                                            uint32_t (*hist)[kBlock], uint32_t (*scratch)[kWaves + 2]) {
+    static_assert(kBins % kThreads == 0 && kBins <= kBlock, "bins per thread");
+    constexpr int per = kBins / kThreads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t prefix[N], rank[N];
 #pragma unroll
-    for (int k = 0; k < N; ++k) { prefix[k] = 0u; rank[k] = rank0; }
-    uint32_t pmask = 0;
-#pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 20 : (pass == 1 ? 9 : 0);
-        const int bits = pass == 2 ? 9 : 11;
-        const int nb = 1 << bits;
-        const int per = nb / kThreads;
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            if (!act[k]) continue;
-            // this thread's `per` adjacent bins, in 16-byte stores
+    for (int k = 0; k < N; ++k) {
+        if (!act[k]) continue;
+        // this thread's `per` adjacent bins, in 16-byte stores where they fit
+        if constexpr (per % 4 == 0) {
             uint4 *h4 = reinterpret_cast<uint4 *>(&hist[k][tid * per]);
 #pragma unroll
-            for (int i = 0; i < kBlock / kThreads / 4; ++i)
-                if (4 * i + 4 <= per) h4[i] = uint4{0u, 0u, 0u, 0u};
-            if (per < 4)
-                for (int i = 0; i < per; ++i) hist[k][tid * per + i] = 0u;
+            for (int i = 0; i < per / 4; ++i) h4[i] = uint4{0u, 0u, 0u, 0u};
+        } else {
+#pragma unroll
+            for (int i = 0; i < per; ++i) hist[k][tid * per + i] = 0u;
         }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            if (!act[k]) continue;
-#pragma unroll
-            for (int i = 0; i < kItems; ++i) {
-                const uint32_t key = __float_as_uint(x[k][i]) & 0x7FFFFFFFu;
-                if ((key & pmask) == prefix[k]) atomicAdd(&hist[k][(key >> shift) & (nb - 1)], 1u);
-            }
-        }
-        __syncthreads();
-        uint32_t mine[N], incl[N];
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            mine[k] = 0u;
-            incl[k] = 0u;
-            if (!act[k]) continue;
-            for (int i = 0; i < per; ++i) mine[k] += hist[k][tid * per + i];
-            incl[k] = wave_inclusive_sum(mine[k]);
-            if (lane == 63) scratch[k][wave] = incl[k];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            if (!act[k]) continue;
-            for (int w = 0; w < wave; ++w) incl[k] += scratch[k][w];
-            const uint32_t excl = incl[k] - mine[k];
-            if (excl <= rank[k] && rank[k] < incl[k]) {
-                // the digit is among this thread's bins: read them at once and
-                // take the first whose running count passes the rank (no chain
-                // of dependent LDS reads while the other waves wait)
-                uint32_t hb[kBlock / kThreads];
-#pragma unroll
-                for (int i = 0; i < kBlock / kThreads; ++i) hb[i] = i < per ? hist[k][tid * per + i] : 0u;
-                uint32_t cum = excl, b = (uint32_t)(tid * per);
-                bool found = false;
-#pragma unroll
-                for (int i = 0; i < kBlock / kThreads; ++i) {
-                    const bool take = !found && i < per && cum + hb[i] <= rank[k];
-                    cum = take ? cum + hb[i] : cum;
-                    b += take ? 1u : 0u;
-                    found = found || !take;
-                }
-                scratch[k][kWaves] = b;
-                scratch[k][kWaves + 1] = rank[k] - cum;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            if (!act[k]) continue;
-            prefix[k] |= scratch[k][kWaves] << shift;
-            rank[k] = scratch[k][kWaves + 1];
-        }
-        pmask |= (uint32_t)(nb - 1) << shift;
     }
+    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < N; ++k) out[k] = prefix[k];
+    for (int k = 0; k < N; ++k) {
+        if (!act[k]) continue;
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) {
+            const uint32_t key = __float_as_uint(x[k][i]) & 0x7FFFFFFFu;
+            if (take(k, key)) atomicAdd(&hist[k][digit(k, key)], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t mine[N], incl[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        mine[k] = 0u;
+        incl[k] = 0u;
+        if (!act[k]) continue;
+#pragma unroll
+        for (int i = 0; i < per; ++i) mine[k] += hist[k][tid * per + i];
+        incl[k] = wave_inclusive_sum(mine[k]);
+        if (lane == 63) scratch[k][wave] = incl[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        if (!act[k]) continue;
+        for (int w = 0; w < wave; ++w) incl[k] += scratch[k][w];
+        const uint32_t excl = incl[k] - mine[k];
+        if (excl <= rank[k] && rank[k] < incl[k]) {
+            // the bin is among this thread's: read them at once and take the
+            // first whose running count passes the rank (no chain of
+            // dependent LDS reads while the other waves wait)
+            uint32_t hb[per];
+#pragma unroll
+            for (int i = 0; i < per; ++i) hb[i] = hist[k][tid * per + i];
+            uint32_t cum = excl, b = (uint32_t)(tid * per);
+            bool found = false;
+#pragma unroll
+            for (int i = 0; i < per; ++i) {
+                const bool step = !found && cum + hb[i] <= rank[k];
+                cum = step ? cum + hb[i] : cum;
+                b += step ? 1u : 0u;
+                found = found || !step;
+            }
+            scratch[k][kWaves] = b;
+            scratch[k][kWaves + 1] = rank[k] - cum;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        if (!act[k]) continue;
+        bin[k] = scratch[k][kWaves];
+        rank[k] = scratch[k][kWaves + 1];
+    }
+}
+
+// rank-th smallest of one moment's 2048 keys by bisection on the key value:
+// the answer is the largest v with at most `rank` keys below v, built bit by
+// bit from the top (31 rounds, each a block-wide count: a compare per key, a
+// DPP wave sum and one barrier, the rounds alternating between two LDS slot
+// rows so that one barrier per round orders them).
+__device__ __forceinline__ uint32_t block_bisect(const float *x, uint32_t rank, uint32_t (*slots)[kWaves]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t lo = 0u;
+#pragma unroll 1
+    for (int bit = 30; bit >= 0; --bit) {
+        const uint32_t cand = lo | (1u << bit);
+        uint32_t c = 0u;
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) c += (__float_as_uint(x[i]) & 0x7FFFFFFFu) < cand ? 1u : 0u;
+        c = wave_inclusive_sum(c);
+        if (lane == 63) slots[bit & 1][wave] = c;
+        __syncthreads();
+        uint32_t total = 0u;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) total += slots[bit & 1][w];
+        if (total <= rank) lo = cand;
+    }
+    return lo;
+}
+
+// rank-th smallest (0-based) of the block's 2048 keys (8 per thread) of each
+// of N moments, by LDS radix select.  top[k] is moment k's largest key (the
+// block maximum, known before the select), E its exponent field.
+//   coarse pass: the digit is the key's binade below E (0..14) and its top 7
+//           mantissa bits: bin = (key >> 16) - ((E - 15) << 7), i.e. 128 +
+//           128 (14 - d) + mantissa for a key d binades below E, clamped to
+//           [127, 2047], so that every key 15 or more binades below E lands
+//           in bin 127 (four instructions per key).  Moments cluster in a
+//           few binades under the block maximum, so 128 bins per binade keep
+//           few keys per bin and few lanes of a wave's atomic add meet on one
+//           LDS word (a digit of the top 11 key bits puts ~80 keys of the
+//           densest binade in one of its 8 bins).  A bin >= 128 fixes the
+//           key's bits 30..16;
+//   fine passes: bits 15..8, then 7..0, of the keys in that bin, 256 bins.
+// When the answer lies in bin 127 (15 binades or more below the maximum:
+// zeros and tiny values, e.g. a low percentile of a block with exact
+// zeros), that moment's statistic comes from block_bisect over all its keys
+// instead.
+template <int N>
+__device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N], const uint32_t (&top)[N],
+                               uint32_t rank0, uint32_t (&out)[N], uint32_t (*hist)[kBlock],
+                               uint32_t (*scratch)[kWaves + 2]) {
+    int32_t base[N];
+    uint32_t rank[N], bin[N], prefix[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        base[k] = ((int32_t)(top[k] >> 23) - 15) * 128;
+        rank[k] = rank0;
+        bin[k] = 0u;
+    }
+    select_pass<N, kBlock>(
+        x, act,
+        [&](int k, uint32_t key) { return (uint32_t)min(max((int32_t)(key >> 16) - base[k], 127), kBlock - 1); },
+        [](int, uint32_t) { return true; }, bin, rank, hist, scratch);
+    bool fine[N], any_low = false;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        fine[k] = act[k] && bin[k] != 127u;
+        any_low = any_low || (act[k] && bin[k] == 127u);
+        prefix[k] = (uint32_t)((int32_t)bin[k] + base[k]) << 16;  // bits 30..16 of the bin's keys
+    }
+    select_pass<N, 256>(
+        x, fine, [](int, uint32_t key) { return (key >> 8) & 255u; },
+        [&](int k, uint32_t key) { return (key & 0x7FFF0000u) == prefix[k]; }, bin, rank, hist, scratch);
+#pragma unroll
+    for (int k = 0; k < N; ++k) prefix[k] |= bin[k] << 8;
+    select_pass<N, 256>(
+        x, fine, [](int, uint32_t key) { return key & 255u; },
+        [&](int k, uint32_t key) { return (key & 0x7FFFFF00u) == prefix[k]; }, bin, rank, hist, scratch);
+#pragma unroll
+    for (int k = 0; k < N; ++k) out[k] = prefix[k] | bin[k];
+    if (any_low) {  // block-uniform; the histograms are free after the last pass's barrier
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            if (act[k] && !fine[k])
+                out[k] = block_bisect(x[k], rank0, reinterpret_cast<uint32_t (*)[kWaves]>(hist[k]));
+    }
 }
 
 // The same statistic when it lies near the top: the rank-th smallest of the
@@ -275,7 +353,7 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
 // (fewer than `need` keys of the block lie above it).
 // Keys are stored plus one, so 0 marks "dropped" / "empty" and the unsigned
 // max with its identity 0 serves both walks.
-constexpr uint32_t kTopCap = 16;  // largest need taken by the walks
+constexpr uint32_t kTopCap = 16;  // entries of a wave's list (the union: one per lane)
 static_assert(kWaves * kTopCap == 64, "one union entry per lane");
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
@@ -324,75 +402,43 @@ __device__ __forceinline__ void wave_top(const float (&x)[kItems], uint32_t need
     }
 }
 
-// The same walk with less work per round: each lane first keeps only its T
-// largest keys, sorted (k[0] >= ... >= k[T-1]), and a round looks at the
-// lanes' heads k[0] only: M = the largest head, counted over the heads
-// equal to it, and those lanes shift their lists up by one.  While every
-// lane still holds a known key, M is the wave's largest remaining key; a
-// value repeated within a lane comes back as M in the next rounds, so it
-// may appear in the list more than once (the merge sums such entries).
-// A lane whose list runs empty may hide more keys at or above the next
-// value: if need is not reached by then, the wave returns false and takes
-// the full walk.  The round that reaches need may miss such hidden copies
-// of M in its count; the merge stays exact, since that count is still at
-// least need, and only the counts above the last value enter its sums
-// below the answer.  T = 2 serves need <= 4 (a wave falls back when one
-// lane holds two of its three largest keys: ~4% of waves for distinct
-// keys), T = 4 serves need <= kTopCap (one lane holding 4 of the wave's 15
-// largest keys: ~0.5% of waves).
-constexpr uint32_t kPairNeed = 4;
+// The same walk with less work per round: each lane first keeps only its two
+// largest keys, sorted (k0 >= k1), and a round looks at the lanes' heads k0
+// only: M = the largest head, counted over the heads equal to it, and those
+// lanes shift their lists up by one.  While every lane still holds a known
+// key, M is the wave's largest remaining key; a value repeated within a lane
+// comes back as M in the next round, so it may appear in the list more than
+// once (the merge sums such entries).  A lane whose list runs empty may hide
+// more keys at or above the next value: if need is not reached by then, the
+// wave returns false and takes the full walk (a wave falls back when one
+// lane holds two of its three largest keys: ~4% of waves for distinct keys).
+// The round that reaches need may miss such hidden copies of M in its count;
+// the merge stays exact, since that count is still at least need, and only
+// the counts above the last value enter its sums below the answer.
+// The walks serve need <= 4 (percentiles of 99.85 and above for a full
+// block, the pages' default 99.9 among them); from need 5 on, the radix
+// select is faster (8-bit ViT-Base set, percentile 99.5 (need 12): 317
+// against 288 Gparams/s for walks over per-lane top-4 lists).
+constexpr uint32_t kWalkNeed = 4;
 
-// The lane's T largest keys, largest first, in k0..k3 (k2 = k3 = 0 for T =
-// 2).  Named registers rather than an array: the compiler turned the shift
-// of an array into an index-compare chain five times as long.
-template <int T>
-__device__ __forceinline__ void lane_top(const float (&x)[kItems], uint32_t &k0, uint32_t &k1, uint32_t &k2,
-                                         uint32_t &k3) {
-    if constexpr (T == 2) {
-        uint32_t a = top_key(x[0]), b = top_key(x[1]);
-        const uint32_t hi = max(a, b);
-        b = min(a, b);
-        a = hi;
-#pragma unroll
-        for (int i = 2; i < kItems; ++i) {
-            const uint32_t y = top_key(x[i]);
-            b = max(b, min(a, y));
-            a = max(a, y);
-        }
-        k0 = a;
-        k1 = b;
-        k2 = 0u;
-        k3 = 0u;
-    } else {
-        static_assert(T == 4 && kItems == 8, "top 4 of 8 keys");
-        // sort each half with a 5-exchange network, keep the top 4 of the
-        // two (a bitonic sequence), sort it with 4 exchanges
-        auto cx = [](uint32_t &p, uint32_t &q) {  // p >= q afterwards
-            const uint32_t hi = max(p, q);
-            q = min(p, q);
-            p = hi;
-        };
-        uint32_t a0 = top_key(x[0]), a1 = top_key(x[1]), a2 = top_key(x[2]), a3 = top_key(x[3]);
-        uint32_t b0 = top_key(x[4]), b1 = top_key(x[5]), b2 = top_key(x[6]), b3 = top_key(x[7]);
-        cx(a0, a1); cx(a2, a3); cx(a0, a2); cx(a1, a3); cx(a1, a2);
-        cx(b0, b1); cx(b2, b3); cx(b0, b2); cx(b1, b3); cx(b1, b2);
-        k0 = max(a0, b3);
-        k1 = max(a1, b2);
-        k2 = max(a2, b1);
-        k3 = max(a3, b0);
-        cx(k0, k2); cx(k1, k3); cx(k0, k1); cx(k2, k3);
-    }
-}
-
-template <int T>
 __device__ __forceinline__ bool wave_top_lanes(const float (&x)[kItems], uint32_t need, uint32_t *val,
                                                uint32_t *cnt) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t k0, k1, k2, k3;
-    lane_top<T>(x, k0, k1, k2, k3);
+    uint32_t k0 = top_key(x[0]), k1 = top_key(x[1]);
+    {
+        const uint32_t hi = max(k0, k1);
+        k1 = min(k0, k1);
+        k0 = hi;
+    }
+#pragma unroll
+    for (int i = 2; i < kItems; ++i) {
+        const uint32_t y = top_key(x[i]);
+        k1 = max(k1, min(k0, y));
+        k0 = max(k0, y);
+    }
     uint32_t my_val = 0u, my_cnt = 0u, acc = 0u;
-    // each round counts at least one key, so kTopCap rounds always reach need
-    for (uint32_t it = 0; it < kTopCap; ++it) {
+    // each round counts at least one key, so kWalkNeed rounds always reach need
+    for (uint32_t it = 0; it < kWalkNeed; ++it) {
         const uint32_t M = wave_max_u32(k0);
         const bool hit = k0 == M;
         const uint32_t C = (uint32_t)__popcll(__ballot(hit));
@@ -400,9 +446,7 @@ __device__ __forceinline__ bool wave_top_lanes(const float (&x)[kItems], uint32_
         acc += C;
         if (acc >= need) break;
         k0 = hit ? k1 : k0;
-        k1 = hit ? k2 : k1;
-        k2 = hit ? k3 : k2;
-        k3 = hit ? 0u : k3;
+        k1 = hit ? 0u : k1;
         if (__ballot(k0 == 0u) != 0) return false;  // a lane without a known key
     }
     if (lane < (int)kTopCap) {
@@ -414,9 +458,7 @@ __device__ __forceinline__ bool wave_top_lanes(const float (&x)[kItems], uint32_
 
 __device__ __forceinline__ void wave_top_any(const float (&x)[kItems], uint32_t need, uint32_t *val,
                                              uint32_t *cnt) {
-    const bool done = need <= kPairNeed ? wave_top_lanes<2>(x, need, val, cnt)
-                                        : wave_top_lanes<4>(x, need, val, cnt);
-    if (!done) wave_top(x, need, val, cnt);
+    if (!wave_top_lanes(x, need, val, cnt)) wave_top(x, need, val, cnt);
 }
 
 // need-th largest key over the union of the wave lists (after a barrier
@@ -588,32 +630,48 @@ __device__ __forceinline__ void load_data(const StepArgs &a, const BlockCtx &c,
                 }
             }
         }
-        // state: padding entries of the segment hold zeros
+        // state: entries past the tensor's end (its 16-element padding) take
+        // no part in the step, whatever a written or loaded state holds
+        // there: in a ragged block they are masked to zero as they arrive
+        // (integer masks, element k of the group kept iff k < live), so
+        // they decode as zero and are stored back as zero
         const size_t s = c.gidx + e0;
         const bool in = kFull || e0 < c.npad;
+        int32_t live = 4;
+        uint32_t keep8 = ~0u, keep16lo = ~0u, keep16hi = ~0u;
+        if constexpr (!kFull) {
+            live = min(max((int32_t)c.n - (int32_t)e0, 0), 4);
+            keep8 = (uint32_t)(0xFFFFFFFFull >> (32 - 8 * live));
+            keep16lo = (uint32_t)(0xFFFFFFFFull >> (32 - 16 * min(live, 2)));
+            keep16hi = (uint32_t)(0xFFFFFFFFull >> (32 - 16 * max(live - 2, 0)));
+        }
         if constexpr (kStore == kStoreBf16) {
             u32x2 hm = {0u, 0u}, hv = {0u, 0u};
             if (in) {
                 hm = ld_u32x2(reinterpret_cast<const uint16_t *>(a.m_state) + s);
                 hv = ld_u32x2(reinterpret_cast<const uint16_t *>(a.v_state) + s);
             }
-            r.m[2 * j] = hm.x; r.m[2 * j + 1] = hm.y;
-            r.v[2 * j] = hv.x; r.v[2 * j + 1] = hv.y;
+            r.m[2 * j] = hm.x & keep16lo; r.m[2 * j + 1] = hm.y & keep16hi;
+            r.v[2 * j] = hv.x & keep16lo; r.v[2 * j + 1] = hv.y & keep16hi;
             if constexpr (kAms) {
                 u32x2 hw = {0u, 0u};
                 if (in) hw = ld_u32x2(reinterpret_cast<const uint16_t *>(a.w_state) + s);
-                r.w[2 * j] = hw.x; r.w[2 * j + 1] = hw.y;
+                r.w[2 * j] = hw.x & keep16lo; r.w[2 * j + 1] = hw.y & keep16hi;
             }
         } else {
-            r.v[j] = in ? ld_u32(reinterpret_cast<const uint8_t *>(a.v_state) + s) : 0u;
-            if constexpr (kAms) r.w[j] = in ? ld_u32(reinterpret_cast<const uint8_t *>(a.w_state) + s) : 0u;
+            r.v[j] = in ? ld_u32(reinterpret_cast<const uint8_t *>(a.v_state) + s) & keep8 : 0u;
+            if constexpr (kAms) r.w[j] = in ? ld_u32(reinterpret_cast<const uint8_t *>(a.w_state) + s) & keep8 : 0u;
             if constexpr (kStore == kStoreQ8) {
-                r.m[j] = in ? ld_u32(reinterpret_cast<const int8_t *>(a.m_state) + s) : 0u;
+                r.m[j] = in ? ld_u32(reinterpret_cast<const int8_t *>(a.m_state) + s) & keep8 : 0u;
             } else {
                 f32x4 mf = {0.f, 0.f, 0.f, 0.f};
                 if (in) mf = ld_f32x4(reinterpret_cast<const float *>(a.m_state) + s);
                 r.m[4 * j + 0] = __float_as_uint(mf.x); r.m[4 * j + 1] = __float_as_uint(mf.y);
                 r.m[4 * j + 2] = __float_as_uint(mf.z); r.m[4 * j + 3] = __float_as_uint(mf.w);
+                if constexpr (!kFull) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) r.m[4 * j + k] &= (uint32_t)((int32_t)(k - live) >> 31);
+                }
             }
         }
     }
@@ -737,21 +795,6 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             }
         }
     }
-    if constexpr (!kFull) {
-        // State entries past the tensor's end (its 16-element padding) take
-        // no part in the step: whatever a written or loaded state holds
-        // there decodes as zero, so the block statistic sees the live
-        // elements and zeros only, and the padding is stored back as zero.
-#pragma unroll
-        for (int i = 0; i < kItems; ++i) {
-            const uint32_t e = (i / 4) * (kThreads * 4) + 4 * tid + (i & 3);
-            if (e >= c.n) {
-                mo[i] = 0.0f;
-                vo[i] = 0.0f;
-                if constexpr (kAms) wo[i] = 0.0f;
-            }
-        }
-    }
 
     // ---- the Adam/AdamW element update (moments stay in registers)
     if (a.l2) {  // Adam with L2-coupled weight decay (uniform branch)
@@ -859,7 +902,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         uint32_t rank = 0, need = 0;
         if constexpr (kPct != kPctNone) {
             rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
-            need = kBlock - rank;  // in [1, kTopCap] for kPctTop (walk_covers)
+            need = kBlock - rank;  // in [1, kWalkNeed] for kPctTop (walk_covers)
         }
         if constexpr (kPct == kPctTop) {  // wave walks; the barrier in block_max publishes their lists
             if (need_m) wave_top_any(mo, need, sel.val[0], sel.cnt[0]);
@@ -903,16 +946,18 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                 if constexpr (kAms) {
                     const float *const xs[3] = {mo, vo, wo};
                     const bool act[3] = {need_m, need_v, need_w};
+                    const uint32_t top[3] = {__float_as_uint(mmax), __float_as_uint(vmax), __float_as_uint(wmax)};
                     uint32_t res[3];
-                    block_select_n<3>(xs, act, rank, res, sel.h, sel.s);
+                    block_select_n<3>(xs, act, top, rank, res, sel.h, sel.s);
                     st[0] = __uint_as_float(res[0]);
                     st[1] = __uint_as_float(res[1]);
                     st[2] = __uint_as_float(res[2]);
                 } else {
                     const float *const xs[2] = {mo, vo};
                     const bool act[2] = {need_m, need_v};
+                    const uint32_t top[2] = {__float_as_uint(mmax), __float_as_uint(vmax)};
                     uint32_t res[2];
-                    block_select_n<2>(xs, act, rank, res, sel.h, sel.s);
+                    block_select_n<2>(xs, act, top, rank, res, sel.h, sel.s);
                     st[0] = __uint_as_float(res[0]);
                     st[1] = __uint_as_float(res[1]);
                 }
@@ -981,11 +1026,26 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 }
 
 // ---------------------------------------------------------------- kernel
+// Waves per SIMD the radix-select variants are compiled for.  Left to
+// itself the compiler spends registers freely there (the select's passes and
+// its bisection fallback) and lands at 4-7 waves per SIMD; asking for one
+// or two more gets them by moving a few scalar registers into vector lanes,
+// with no memory spills (checked per variant; the stochastic-rounding
+// AMSGrad variants would spill and keep the compiler's choice).  8-bit
+// ViT-Base set at percentile 99.0: 317 Gparams/s at 8 waves against 309 at
+// 7.
+constexpr int select_waves(int store, bool sr, int pct, bool ams) {
+    if (pct != 2 || (sr && ams)) return 1;
+    if (store == kStoreQ8) return !sr && !ams ? 8 : (sr ? 7 : 6);
+    return !sr && !ams ? 7 : 6;
+}
+
 // One workgroup per block; workgroups beyond the grid limit loop (stride =
 // grid size).  Descriptors [0, n_full) are full blocks, whose path has no
 // tail checks; the rest are the tensors' ragged last blocks.
 template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAms>
-__global__ void __launch_bounds__(kThreads) adam_step_kernel(StepArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(select_waves(kStore, kSR, kPct, kAms))))
+adam_step_kernel(StepArgs a) {
     __shared__ BlockLds lds;
     __shared__ SelectLds<kPct, kAms ? 3 : 2> sel;
     for (uint32_t i0 = blockIdx.x; i0 < a.n_all; i0 += gridDim.x) {
@@ -1053,12 +1113,12 @@ hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// The walks serve a step when every block's need is at most kTopCap.  need =
+// The walks serve a step when every block's need is at most kWalkNeed.  need =
 // n - floor(p (n - 1)) for a block of n values never falls as n grows (n + 1
 // raises the floor by 0 or 1), so the full block's need decides; the double
 // arithmetic is the kernel's own, so both sides agree on it.
 bool walk_covers(double pfrac) {
-    return (uint32_t)kBlock - (uint32_t)floor(pfrac * (double)(kBlock - 1)) <= kTopCap;
+    return (uint32_t)kBlock - (uint32_t)floor(pfrac * (double)(kBlock - 1)) <= kWalkNeed;
 }
 
 template <int kStore, bool kGradBf16, bool kSR, bool kStatic, bool kAms>
