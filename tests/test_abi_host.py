@@ -317,3 +317,34 @@ def test_noalloc_limits_refused_before_any_device_call():
                                    ctypes.cast(ptrs, ctypes.c_void_p),
                                    ctypes.cast(state, ctypes.c_void_p), None, ctypes.byref(hp), None)
         assert rc == -1 and what in lib.adam_last_error(), lib.adam_last_error()
+
+
+def test_step_checks_rerun_when_tensors_change(monkeypatch):
+    # the binding checks a call's tensors in full when the tensor objects or
+    # their data pointers differ from the last checked call on the state,
+    # and only compares identities and pointers otherwise
+    import torch
+    st = _fake_state([100, 7])
+    full = []
+    monkeypatch.setattr(B, "_check_step_tensors", lambda s, p, g: full.append(1))
+    ps = [torch.zeros(100), torch.zeros(7)]
+    gs = [torch.zeros(100), torch.zeros(7)]
+    for _ in range(3):
+        B._checked_pointers(st, ps, gs)
+    assert len(full) == 1
+    B._checked_pointers(st, list(ps), list(gs))  # new lists, same tensors
+    assert len(full) == 1
+    gs2 = [gs[0], torch.zeros(7)]  # one new tensor object
+    B._checked_pointers(st, ps, gs2)
+    assert len(full) == 2
+    ps[1].set_(torch.zeros(7).untyped_storage())  # same object, new data pointer
+    B._checked_pointers(st, ps, gs2)
+    assert len(full) == 3
+    # rotating a few gradient sets stays on the fast path
+    sets = [[torch.zeros(100), torch.zeros(7)] for _ in range(4)]
+    for r in range(12):
+        B._checked_pointers(st, ps, sets[r % 4])
+    assert len(full) == 3 + 4
+    st.destroy()
+    B._checked_pointers(st, ps, gs2)  # a destroyed state forgets
+    assert len(full) == 8
