@@ -41,8 +41,8 @@
  * Philox4x32-10, key = seed, counter = (draw index / 4, t), word = draw
  * index mod 4 -- the draw index being the flat index unless set otherwise
  * (adam_state_set_draw_index) -- low half for m and high half for v; the
- * AMSGrad maximum takes the low half of the word at counter (draw index / 4
- * + 2^63, t)) and
+ * AMSGrad maximum draws one Philox call per 8 elements: half (i mod 2) of
+ * word (i / 2) mod 4 at counter (i / 8 + 2^63, t) for draw index i) and
  * pins |x| >= A to qmax; a block with A < 2^-112 stores zero codes and
  * scale 0.  The AMSGrad maximum is stored as v is: bf16, or uint8 codes
  * with their own per-block scale.

@@ -977,6 +977,32 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         const float pin_v = vzero ? __builtin_inff() : Avn;
         const float pin_w = wzero ? __builtin_inff() : Awn;
 
+        // ---- the AMSGrad maximum's draws (stochastic rounding): one Philox
+        // call per 8 elements, on the counter stream with bit 63 set; element
+        // i takes half i mod 2 of word (i / 2) mod 4 at counter i / 8.  The
+        // lanes of a pair (2m, 2m + 1) hold the two halves of one 8-element
+        // group of each of their 4-element groups: the even lane computes
+        // the call of their first group, the odd lane that of their second,
+        // and one DPP swap hands each lane the two words it lacks.  Every
+        // lane takes part (the swap reads its partner): an 8-element group
+        // lies wholly inside or wholly past a tensor's 16-padded segment.
+        static_assert(kGroups == 2, "a lane pair's two 4-element groups");
+        uint32_t wdraw[kGroups][2] = {};
+        if constexpr (kSR && kAms) {
+            const bool odd = (tid & 1) != 0;
+            const uint64_t g8 = (c.didx >> 3) + (odd ? (uint64_t)(kThreads * 4 / 8) : 0u) + (uint64_t)(tid >> 1);
+            uint32_t ctr[4] = {(uint32_t)g8, (uint32_t)(g8 >> 32) | 0x80000000u, a.t_lo, a.t_hi};
+            philox4x32_10(ctr, a.seed_lo, a.seed_hi);
+            // the even lane lacks words 0, 1 of the second group's call, the
+            // odd lane words 2, 3 of the first group's
+            const uint32_t got0 = dpp<kQuadPerm1032>(odd ? ctr[0] : ctr[2]);
+            const uint32_t got1 = dpp<kQuadPerm1032>(odd ? ctr[1] : ctr[3]);
+            wdraw[0][0] = odd ? got0 : ctr[0];
+            wdraw[0][1] = odd ? got1 : ctr[1];
+            wdraw[1][0] = odd ? ctr[2] : got0;
+            wdraw[1][1] = odd ? ctr[3] : got1;
+        }
+
         // ---- requantize and store codes
 #pragma unroll
         for (int j = 0; j < kGroups; ++j) {
@@ -990,10 +1016,10 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                 philox4x32_10(ctr, a.seed_lo, a.seed_hi);
                 rnd[0] = ctr[0]; rnd[1] = ctr[1]; rnd[2] = ctr[2]; rnd[3] = ctr[3];
                 if constexpr (kAms) {
-                    // the maximum's draws: the counter stream with bit 63 set
-                    uint32_t ctr_w[4] = {(uint32_t)grp, (uint32_t)(grp >> 32) | 0x80000000u, a.t_lo, a.t_hi};
-                    philox4x32_10(ctr_w, a.seed_lo, a.seed_hi);
-                    rnd_w[0] = ctr_w[0]; rnd_w[1] = ctr_w[1]; rnd_w[2] = ctr_w[2]; rnd_w[3] = ctr_w[3];
+                    rnd_w[0] = wdraw[j][0];
+                    rnd_w[1] = wdraw[j][0] >> 16;
+                    rnd_w[2] = wdraw[j][1];
+                    rnd_w[3] = wdraw[j][1] >> 16;
                 }
             }
             st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s, pack_u8<kSR>(vo, 4 * j, pin_v, rv, rnd, 16));

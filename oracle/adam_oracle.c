@@ -129,21 +129,32 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
    counter = (lo32(c), hi32(c), lo32 t, hi32 t), c = i/4.  The first moment
    (which 0) uses the low 16 bits of that word, the second moment (which 1)
    the high 16 bits.  The running maximum of the second moment (AMSGrad,
-   which 2) uses the low 16 bits of the word at c = i/4 + 2^63: flat indices
-   stay below 2^62, so its counters never meet the first stream's. */
+   which 2) draws from a second stream, one Philox call per 8 elements:
+   element i takes half (i mod 2) -- the low 16 bits for even i, the high 16
+   for odd i -- of word ((i/2) mod 4) at counter c = i/8 + 2^63 (flat
+   indices stay below 2^62, so these counters never meet the first
+   stream's). */
 void orc_sr_draws(uint64_t seed, int64_t t, int64_t gidx0, int64_t n,
                   int32_t which, uint16_t *out)
 {
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     for (int64_t j = 0; j < n; j++) {
         const uint64_t i = (uint64_t)(gidx0 + j);
-        const uint64_t grp = (i >> 2) | (which == 2 ? (1ull << 63) : 0ull);
+        const uint64_t grp = which == 2 ? ((i >> 3) | (1ull << 63)) : (i >> 2);
         const uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32),
                                  (uint32_t)(uint64_t)t, (uint32_t)((uint64_t)t >> 32)};
         uint32_t w[4];
         orc_philox4x32_10(ctr, key, w);
-        const uint32_t word = w[i & 3u];
-        out[j] = (uint16_t)(which == 1 ? (word >> 16) : (word & 0xFFFFu));
+        uint32_t half_hi;
+        uint32_t word;
+        if (which == 2) {
+            word = w[(i >> 1) & 3u];
+            half_hi = (uint32_t)(i & 1u);
+        } else {
+            word = w[i & 3u];
+            half_hi = which == 1;
+        }
+        out[j] = (uint16_t)(half_hi ? (word >> 16) : (word & 0xFFFFu));
     }
 }
 

@@ -106,18 +106,20 @@ def philox_ref(tmp_path_factory):
 
 
 def test_maximum_draws_use_the_second_counter_stream(orc, philox_ref):
-    # element i at step t: word (i mod 4) of philox(seed, subsequence=t,
-    # offset=i/4 + 2^63), low half
+    # element i at step t: half (i mod 2) of word ((i/2) mod 4) of
+    # philox(seed, subsequence=t, offset=i/8 + 2^63): one call per 8 elements
     for seed, t, gidx0 in [(42, 1, 0), (1234, 5, 2 ** 33 + 12), (7, 3, 2046)]:
         n = 40
         idx = np.arange(gidx0, gidx0 + n, dtype=np.uint64)
-        groups = sorted(set(int(i) >> 2 for i in idx))
+        groups = sorted(set(int(i) >> 3 for i in idx))
         words = dict(zip(groups, philox_ref([(seed, t, g + 2 ** 63) for g in groups])))
         got = orc.sr_draws(seed, t, gidx0, n, 2)
         for j, i in enumerate(idx):
-            assert got[j] == int(words[int(i) >> 2][int(i) & 3]) & 0xFFFF
-        # and it is not the first stream's
+            i = int(i)
+            assert got[j] == (int(words[i >> 3][(i >> 1) & 3]) >> (16 * (i & 1))) & 0xFFFF
+        # and it is not the first stream's, in either half
         assert not np.array_equal(got, orc.sr_draws(seed, t, gidx0, n, 0))
+        assert not np.array_equal(got, orc.sr_draws(seed, t, gidx0, n, 1))
 
 
 @pytest.mark.parametrize("storage", ["q8", "q8_v_only"])

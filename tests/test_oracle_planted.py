@@ -8,6 +8,8 @@ Mistakes planted (one per build):
                 ties to even
   recip_128     codebook step 1/128 instead of 1/qmax
   draw_halves   first and second moment take each other's 16-bit draw halves
+  max_draw_word the AMSGrad maximum's draws from word i mod 4 instead of
+                (i / 2) mod 4
   eps_in_root   eps added under the square root instead of after it
   rank_ceil     percentile entry ceil(p/100 (n-1)) instead of floor
   no_omb1       first-moment EMA without the (1 - beta1) factor
@@ -28,14 +30,14 @@ SOURCE = os.path.join(ROOT, "oracle", "adam_oracle.c")
 pytestmark = pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
 
 PIN_TESTS = ["tests/test_oracle_encodings.py", "tests/test_oracle_quant.py",
-             "tests/test_oracle_adam.py", "tests/test_golden.py"]
+             "tests/test_oracle_adam.py", "tests/test_oracle_amsgrad.py", "tests/test_golden.py"]
 
 # (name, exact source text, replacement)
 MUTATIONS = [
     ("tie_away", "k = (int32_t)rintf(y);", "k = (int32_t)roundf(y);"),
     ("recip_128", "const float R = 1.0f / qmax;", "const float R = 1.0f / 128.0f;"),
-    ("draw_halves", "(which == 1 ? (word >> 16) : (word & 0xFFFFu))",
-     "(which == 1 ? (word & 0xFFFFu) : (word >> 16))"),
+    ("draw_halves", "half_hi = which == 1;", "half_hi = which != 1;"),
+    ("max_draw_word", "word = w[(i >> 1) & 3u];", "word = w[i & 3u];"),
     ("eps_in_root", "fmaf(sqrtf(w), ibc2, h->eps)", "fmaf(sqrtf(w + h->eps), ibc2, 0.0f)"),
     ("rank_ceil", "return (int64_t)floor(frac * (double)(n - 1));",
      "return (int64_t)ceil(frac * (double)(n - 1));"),
