@@ -176,7 +176,11 @@ int adam_state_create(adam_state **out, int32_t n_tensors, const int64_t *numels
 /*
  * One Adam/AdamW step over every tensor of the state, enqueued on
  * hip_stream as a single kernel launch (one 256-thread workgroup per
- * 2048-element block).
+ * 2048-element block).  The operation is the loop body of the 8-bit Adam
+ * page's walkthrough sequence diagram (dequantize m and v, the Adam update
+ * with bias correction, quantize m and v), fused into one pass over memory
+ * as the BF16-Adam page's "The real fix" section asks for the bf16-moment
+ * step; the layout check is that page's drift-detection review comment.
  *   params[k]: device float[numel_k], updated in place;
  *   grads[k]:  device float[numel_k] or bf16 (uint16)[numel_k] per the
  *              layout's grad_dtype, read only;
@@ -205,7 +209,10 @@ int64_t adam_state_buffer_bytes(const adam_state *s, int32_t which);
  * Copies a whole state buffer to dst (device or host memory, caller-owned),
  * or overwrites it from src, asynchronously on hip_stream; nbytes must equal
  * adam_state_buffer_bytes(s, which).  Used for inspection, checkpoints and
- * tests.  Errors: EINVAL (unknown/absent buffer, size mismatch, NULL
+ * tests: the 8-bit Adam page's PR description lists full serialization
+ * support among its key features, beside block-wise quantization with a
+ * scale per block; these calls expose the state's buffers (codes, scales or
+ * moments) one at a time.  Errors: EINVAL (unknown/absent buffer, size mismatch, NULL
  * pointer), EDEVICE.
  */
 int adam_state_read(adam_state *s, int32_t which, void *dst, int64_t nbytes, void *hip_stream);
