@@ -511,7 +511,8 @@ __device__ __forceinline__ uint32_t top_merge(const uint32_t *val, const uint32_
 // Stochastic rounding: floor(y) + [u16 * 2^-16 < frac(y)] is computed as
 // (ceil(y * 2^16) + 65535 - u16) >> 16.  With Y = y * 2^16 (exact, Y < 2^24)
 // = 2^16 floor(y) + F, u16 < F holds iff u16 < ceil(F), iff the low 16 bits of
-// ceil(Y) + 65535 - u16 carry into bit 16.
+// ceil(Y) + 65535 - u16 carry into bit 16.  Callers pass nu16 = 65535 - u16,
+// taken from the complement of the draw word: one NOT serves both halves.
 enum EndRule { kNoEnd, kPinEnd, kClampEnd };
 
 // floor(x) converted to int32 in one instruction (the compiler emits a floor
@@ -524,13 +525,13 @@ __device__ __forceinline__ int32_t cvt_floor(float x) {
 }
 
 template <bool kSR, EndRule kEnd>
-__device__ __forceinline__ uint32_t code_magnitude(float a, float A, float r, uint32_t qmax, uint32_t u16) {
+__device__ __forceinline__ uint32_t code_magnitude(float a, float A, float r, uint32_t qmax, uint32_t nu16) {
     float y = a * r;
     if constexpr (kEnd == kClampEnd) y = fminf(y, (float)qmax);
     uint32_t k;
     if constexpr (kSR) {
         // ceil(Y) = -floor(-Y): one convert and one subtract
-        k = ((0xFFFFu - u16) - (uint32_t)cvt_floor(y * -65536.0f)) >> 16;
+        k = (nu16 - (uint32_t)cvt_floor(y * -65536.0f)) >> 16;
     } else {
         k = (uint32_t)rintf(y);
     }
@@ -735,17 +736,17 @@ __device__ __forceinline__ float div_rn(float n, float d) {
 }
 
 // Codes of four unsigned values x[b..b+3] (v, or the AMSGrad maximum) packed
-// into the bytes of one word; u: the group's four Philox words, of which the
-// 16 bits at `shift` are the draws.
+// into the bytes of one word; nu: the complements of the group's four Philox
+// words, of which the 16 bits at `shift` are the complemented draws.
 template <bool kSR>
 __device__ __forceinline__ uint32_t pack_u8(const float (&x)[kItems], int b, float pin, float r,
-                                            const uint32_t (&u)[4], int shift) {
+                                            const uint32_t (&nu)[4], int shift) {
     uint32_t c = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float ax = fabsf(x[b + k]);
         if constexpr (kSR) {
-            c |= code_magnitude<true, kPinEnd>(ax, pin, r, 255u, (u[k] >> shift) & 0xFFFFu) << (8 * k);
+            c |= code_magnitude<true, kPinEnd>(ax, pin, r, 255u, (nu[k] >> shift) & 0xFFFFu) << (8 * k);
         } else {
             // nearest-even rounding, clamped to [0, 255], packed into byte k: the
             // clamp is the end pin (|x| >= A gives y >= 254.99998)
@@ -1014,12 +1015,20 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                 const uint64_t grp = (c.didx + e0) >> 2;  // draw index / 4
                 uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), a.t_lo, a.t_hi};
                 philox4x32_10(ctr, a.seed_lo, a.seed_hi);
-                rnd[0] = ctr[0]; rnd[1] = ctr[1]; rnd[2] = ctr[2]; rnd[3] = ctr[3];
+                // complemented draws (65535 - u16 in each half); the empty asm
+                // keeps each complement in a register, where both halves'
+                // subtractions read it (left visible, the compiler re-derives
+                // the low half's complement from the word: one more op)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    rnd[k] = ~ctr[k];
+                    asm("" : "+v"(rnd[k]));
+                }
                 if constexpr (kAms) {
-                    rnd_w[0] = wdraw[j][0];
-                    rnd_w[1] = wdraw[j][0] >> 16;
-                    rnd_w[2] = wdraw[j][1];
-                    rnd_w[3] = wdraw[j][1] >> 16;
+                    rnd_w[0] = ~wdraw[j][0];
+                    rnd_w[1] = ~wdraw[j][0] >> 16;
+                    rnd_w[2] = ~wdraw[j][1];
+                    rnd_w[3] = ~wdraw[j][1] >> 16;
                 }
             }
             st_u32(reinterpret_cast<uint8_t *>(a.v_state) + s, pack_u8<kSR>(vo, 4 * j, pin_v, rv, rnd, 16));
