@@ -133,6 +133,17 @@ __device__ __forceinline__ float wave_max(float x) {
     return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), 63));
 }
 
+// Max over the wave of unsigned values, as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, dpp<kQuadPerm1032>(x));
+    x = max(x, dpp<kQuadPerm2301>(x));
+    x = max(x, dpp<kRowRor4>(x));
+    x = max(x, dpp<kRowRor8>(x));
+    x = max(x, dpp<kRowBcast15, 0xA>(x));
+    x = max(x, dpp<kRowBcast31, 0xC>(x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     uint32_t v = x + dpp<kRowShr1>(x);
@@ -165,17 +176,27 @@ __device__ __forceinline__ void block_max(float (&x)[N], float (*red)[kWaves]) {
     }
 }
 
+// Per-moment LDS scratch row of the select: [0, kWaves) the waves' partial
+// sums (or partial maxima), [kWaves] the chosen bin, [kWaves + 1] the rank
+// within it, [kWaves + 2] the bin's count; 8 words, so that each half is
+// one 16-byte read.
+constexpr int kSelRow = 8;
+static_assert(kWaves == 4, "a row's first half holds the four waves' partials");
+
 // One counting pass of the block select over N moments at once (one
 // histogram each, so the moments share the pass's four barriers): counts
 // digit(k, key) over the keys of moment k with take(k, key), then finds the
-// bin holding the rank[k]-th smallest of them; bin[k] and rank[k] (now the
-// rank within that bin) come back block-uniform.  act[k] (block-uniform)
-// skips moment k.  Keys are |x| as bit patterns (the order of non-negative
-// floats).
+// bin holding the rank[k]-th smallest of them; bin[k], rank[k] (now the
+// rank within that bin) and count[k] (the keys in that bin) come back
+// block-uniform.  act[k] (block-uniform) skips moment k.  Keys are |x| as
+// bit patterns (the order of non-negative floats); digit(k, key) returns the
+// bin's byte offset in the histogram (4 x the bin), so that the address is
+// the digit itself.
 template <int N, int kBins, class Digit, class Take>
 __device__ __forceinline__ void select_pass(const float *const (&x)[N], const bool (&act)[N], Digit digit,
                                             Take take, uint32_t (&bin)[N], uint32_t (&rank)[N],
-                                            uint32_t (*hist)[kBlock], uint32_t (*scratch)[kWaves + 2]) {
+                                            uint32_t (&count)[N], uint32_t (*hist)[kBlock],
+                                            uint32_t (*scratch)[kSelRow]) {
     static_assert(kBins % kThreads == 0 && kBins <= kBlock, "bins per thread");
     constexpr int per = kBins / kThreads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -199,7 +220,7 @@ __device__ __forceinline__ void select_pass(const float *const (&x)[N], const bo
 #pragma unroll
         for (int i = 0; i < kItems; ++i) {
             const uint32_t key = __float_as_uint(x[k][i]) & 0x7FFFFFFFu;
-            if (take(k, key)) atomicAdd(&hist[k][digit(k, key)], 1u);
+            if (take(k, key)) atomicAdd(reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(hist[k]) + digit(k, key)), 1u);
         }
     }
     __syncthreads();
@@ -218,7 +239,9 @@ __device__ __forceinline__ void select_pass(const float *const (&x)[N], const bo
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         if (!act[k]) continue;
-        for (int w = 0; w < wave; ++w) incl[k] += scratch[k][w];
+        // the earlier waves' totals, all four read at once (wave-uniform selects)
+        const uint4 part = *reinterpret_cast<const uint4 *>(&scratch[k][0]);
+        incl[k] += (wave > 0 ? part.x : 0u) + (wave > 1 ? part.y : 0u) + (wave > 2 ? part.z : 0u);
         const uint32_t excl = incl[k] - mine[k];
         if (excl <= rank[k] && rank[k] < incl[k]) {
             // the bin is among this thread's: read them at once and take the
@@ -236,16 +259,61 @@ __device__ __forceinline__ void select_pass(const float *const (&x)[N], const bo
                 b += step ? 1u : 0u;
                 found = found || !step;
             }
-            scratch[k][kWaves] = b;
-            scratch[k][kWaves + 1] = rank[k] - cum;
+            *reinterpret_cast<uint4 *>(&scratch[k][kWaves]) = uint4{b, rank[k] - cum, hist[k][b], 0u};
         }
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         if (!act[k]) continue;
-        bin[k] = scratch[k][kWaves];
-        rank[k] = scratch[k][kWaves + 1];
+        // block-uniform: scalar registers (as vector values they crowd the
+        // kernel's vector registers into spills)
+        const uint4 res = *reinterpret_cast<const uint4 *>(&scratch[k][kWaves]);
+        bin[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.x);
+        rank[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.y);
+        count[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.z);
+    }
+}
+
+// The answer when it is the largest or the smallest key of its bin (the
+// rank within the bin is count - 1, or 0), in one barrier.  A bin is a key
+// range [lo, hi) (its prefix, then every lower bit), and the bins below it
+// and above it hold the other keys, so
+//   largest of the bin  = largest key below hi: the largest u = key - hi
+//                         (unsigned, mod 2^32; keys below hi give u >= 2^31,
+//                         the others u < 2^31);
+//   smallest of the bin = smallest key at or above lo: the largest
+//                         u = lo - 1 - key = ~key + lo (keys >= lo give
+//                         u >= 2^31).
+// Both are u = (key ^ s) + c (one v_xad_u32), and a block maximum of u with
+// identity 0 finds it; key = (u - c) ^ s.
+template <int N>
+__device__ __forceinline__ void block_end_pick(const float *const (&x)[N], const bool (&end)[N],
+                                               const uint32_t (&lo)[N], const uint32_t (&width)[N],
+                                               const uint32_t (&rank)[N], const uint32_t (&count)[N],
+                                               uint32_t (&out)[N], uint32_t (*scratch)[kSelRow]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t sx[N], c[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const bool largest = rank[k] + 1u == count[k];
+        sx[k] = largest ? 0u : 0xFFFFFFFFu;
+        c[k] = largest ? 0u - (lo[k] + width[k]) : lo[k];
+        if (!end[k]) continue;
+        uint32_t u[kItems];
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) u[i] = ((__float_as_uint(x[k][i]) & 0x7FFFFFFFu) ^ sx[k]) + c[k];
+        uint32_t best = max(max(max(u[0], u[1]), max(u[2], u[3])), max(max(u[4], u[5]), max(u[6], u[7])));
+        best = wave_max_u32(best);
+        if (lane == 0) scratch[k][wave] = best;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        if (!end[k]) continue;
+        const uint4 part = *reinterpret_cast<const uint4 *>(&scratch[k][0]);
+        const uint32_t m = max(max(part.x, part.y), max(part.z, part.w));
+        out[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)((m - c[k]) ^ sx[k]));
     }
 }
 
@@ -281,56 +349,95 @@ __device__ __forceinline__ uint32_t block_bisect(const float *x, uint32_t rank, 
 //           mantissa bits: bin = (key >> 16) - ((E - 15) << 7), i.e. 128 +
 //           128 (14 - d) + mantissa for a key d binades below E, clamped to
 //           [127, 2047], so that every key 15 or more binades below E lands
-//           in bin 127 (four instructions per key).  Moments cluster in a
-//           few binades under the block maximum, so 128 bins per binade keep
-//           few keys per bin and few lanes of a wave's atomic add meet on one
-//           LDS word (a digit of the top 11 key bits puts ~80 keys of the
-//           densest binade in one of its 8 bins).  A bin >= 128 fixes the
-//           key's bits 30..16;
+//           in bin 127 (four instructions per key: extract, subtract,
+//           clamp, and the shift to a byte offset).  Moments cluster in a few binades under the block maximum, so 128
+//           bins per binade keep few keys per bin and few lanes of a wave's
+//           atomic add meet on one LDS word (a digit of the top 11 key bits
+//           puts ~80 keys of the densest binade in one of its 8 bins).  A bin
+//           >= 128 fixes the key's bits 30..16;
 //   fine passes: bits 15..8, then 7..0, of the keys in that bin, 256 bins.
-// When the answer lies in bin 127 (15 binades or more below the maximum:
-// zeros and tiny values, e.g. a low percentile of a block with exact
-// zeros), that moment's statistic comes from block_bisect over all its keys
-// instead.
+// After the coarse pass and after the first fine pass, a moment whose answer
+// is the largest or the smallest key of its bin (rank count - 1 or 0: a
+// bin holding one or two keys, or the end of a longer one) skips the rest
+// and takes it by block_end_pick; the moments still undecided run the next
+// pass.  When the answer lies in bin 127 (15 binades or more below the
+// maximum: zeros and tiny values, e.g. a low percentile of a block with
+// exact zeros), that moment's statistic comes from block_bisect over all its
+// keys instead.
 template <int N>
 __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N], const uint32_t (&top)[N],
                                uint32_t rank0, uint32_t (&out)[N], uint32_t (*hist)[kBlock],
-                               uint32_t (*scratch)[kWaves + 2]) {
+                               uint32_t (*scratch)[kSelRow]) {
+    // stage of each moment (block-uniform): 0 done or inactive, 1 bisection,
+    // 2 end pick, 3 next counting pass
     int32_t base[N];
-    uint32_t rank[N], bin[N], prefix[N];
+    uint32_t rank[N], bin[N], count[N], pfx[N], mask[N], stage[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         base[k] = ((int32_t)(top[k] >> 23) - 15) * 128;
         rank[k] = rank0;
         bin[k] = 0u;
+        count[k] = 0u;
+        out[k] = 0u;
     }
     select_pass<N, kBlock>(
         x, act,
-        [&](int k, uint32_t key) { return (uint32_t)min(max((int32_t)(key >> 16) - base[k], 127), kBlock - 1); },
-        [](int, uint32_t) { return true; }, bin, rank, hist, scratch);
-    bool fine[N], any_low = false;
+        [&](int k, uint32_t key) {
+            return (uint32_t)min(max((int32_t)(key >> 16) - base[k], 127), kBlock - 1) * 4u;
+        },
+        [](int, uint32_t) { return true; }, bin, rank, count, hist, scratch);
+    bool more[N], any = false;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-        fine[k] = act[k] && bin[k] != 127u;
-        any_low = any_low || (act[k] && bin[k] == 127u);
-        prefix[k] = (uint32_t)((int32_t)bin[k] + base[k]) << 16;  // bits 30..16 of the bin's keys
+        pfx[k] = (uint32_t)((int32_t)bin[k] + base[k]) << 16;  // bits 30..16 of the bin's keys
+        mask[k] = 0x7FFF0000u;
+        stage[k] = !act[k] ? 0u : bin[k] == 127u ? 1u : (rank[k] == 0u || rank[k] + 1u == count[k]) ? 2u : 3u;
+        more[k] = stage[k] == 3u;
+        any = any || more[k];
     }
-    select_pass<N, 256>(
-        x, fine, [](int, uint32_t key) { return (key >> 8) & 255u; },
-        [&](int k, uint32_t key) { return (key & 0x7FFF0000u) == prefix[k]; }, bin, rank, hist, scratch);
+    if (any) {  // block-uniform
+        select_pass<N, 256>(
+            x, more, [](int, uint32_t key) { return (key >> 6) & (255u << 2); },
+            [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; }, bin, rank, count, hist, scratch);
+        any = false;
 #pragma unroll
-    for (int k = 0; k < N; ++k) prefix[k] |= bin[k] << 8;
-    select_pass<N, 256>(
-        x, fine, [](int, uint32_t key) { return key & 255u; },
-        [&](int k, uint32_t key) { return (key & 0x7FFFFF00u) == prefix[k]; }, bin, rank, hist, scratch);
+        for (int k = 0; k < N; ++k) {
+            if (more[k]) {
+                pfx[k] |= bin[k] << 8;  // bits 30..8
+                mask[k] = 0x7FFFFF00u;
+                stage[k] = (rank[k] == 0u || rank[k] + 1u == count[k]) ? 2u : 3u;
+            }
+            more[k] = stage[k] == 3u;
+            any = any || more[k];
+        }
+        if (any) {
+            select_pass<N, 256>(
+                x, more, [](int, uint32_t key) { return (key << 2) & (255u << 2); },
+                [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; }, bin, rank, count, hist, scratch);
 #pragma unroll
-    for (int k = 0; k < N; ++k) out[k] = prefix[k] | bin[k];
-    if (any_low) {  // block-uniform; the histograms are free after the last pass's barrier
-#pragma unroll
-        for (int k = 0; k < N; ++k)
-            if (act[k] && !fine[k])
-                out[k] = block_bisect(x[k], rank0, reinterpret_cast<uint32_t (*)[kWaves]>(hist[k]));
+            for (int k = 0; k < N; ++k)
+                if (more[k]) out[k] = pfx[k] | bin[k];
+        }
     }
+    // the last pass's final barrier ordered every read of the partial-sum
+    // words before the end pick's writes to them
+    bool end[N];
+    any = false;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        end[k] = stage[k] == 2u;
+        any = any || end[k];
+    }
+    if (any) {
+        uint32_t width[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) width[k] = (~mask[k] & 0x7FFFFFFFu) + 1u;  // keys of one bin
+        block_end_pick<N>(x, end, pfx, width, rank, count, out, scratch);
+    }
+    // the histograms are free after the last pass's barrier
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        if (stage[k] == 1u) out[k] = block_bisect(x[k], rank0, reinterpret_cast<uint32_t (*)[kWaves]>(hist[k]));
 }
 
 // The same statistic when it lies near the top: the rank-th smallest of the
@@ -356,15 +463,6 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
 constexpr uint32_t kTopCap = 16;  // entries of a wave's list (the union: one per lane)
 static_assert(kWaves * kTopCap == 64, "one union entry per lane");
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-    x = max(x, dpp<kQuadPerm1032>(x));
-    x = max(x, dpp<kQuadPerm2301>(x));
-    x = max(x, dpp<kRowRor4>(x));
-    x = max(x, dpp<kRowRor8>(x));
-    x = max(x, dpp<kRowBcast15, 0xA>(x));
-    x = max(x, dpp<kRowBcast31, 0xC>(x));
-    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-}
 
 __device__ __forceinline__ uint32_t top_key(float x) { return (__float_as_uint(x) & 0x7FFFFFFFu) + 1u; }
 
@@ -699,7 +797,7 @@ struct SelectLds<kPctTop, kN> {  // wave lists of the walks (m, v, AMSGrad maxim
 template <int kN>
 struct SelectLds<kPctRadix, kN> {  // one histogram + scan scratch per moment
     alignas(16) uint32_t h[kN][kBlock];  // 16-byte aligned rows: cleared in 16-byte stores
-    uint32_t s[kN][kWaves + 2];
+    alignas(16) uint32_t s[kN][kSelRow];
 };
 
 // ---------------------------------------------------------------- exact sqrt / divide
