@@ -156,10 +156,27 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     return v;
 }
 
+// threadIdx.x as a value computed here: LDS addresses derived from it are
+// then formed where they are used instead of being hoisted out of the block
+// loop and held in vector registers through the whole step.
+__device__ __forceinline__ int local_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// A zero 16-byte vector made where it is stored (a constant one is hoisted
+// out of the block loop, where its four registers get spilled).
+__device__ __forceinline__ uint4 zero4() {
+    uint32_t z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return uint4{z, z, z, z};
+}
+
 // Block-wide max of N non-negative values per thread (one barrier).
 template <int N>
 __device__ __forceinline__ void block_max(float (&x)[N], float (*red)[kWaves]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = local_tid(), lane = t & 63, wave = t >> 6;
 #pragma unroll
     for (int i = 0; i < N; ++i) x[i] = wave_max(x[i]);
     if (kWaves == 1) return;
@@ -177,102 +194,88 @@ __device__ __forceinline__ void block_max(float (&x)[N], float (*red)[kWaves]) {
 }
 
 // Per-moment LDS scratch row of the select: [0, kWaves) the waves' partial
-// sums (or partial maxima), [kWaves] the chosen bin, [kWaves + 1] the rank
-// within it, [kWaves + 2] the bin's count; 8 words, so that each half is
-// one 16-byte read.
+// maxima of the end pick (or bisection counts), [kWaves] the chosen bin,
+// [kWaves + 1] the rank within it, [kWaves + 2] the bin's count; 8 words, so
+// that each half is one 16-byte access.
 constexpr int kSelRow = 8;
+constexpr int kFineBins = 256;
 static_assert(kWaves == 4, "a row's first half holds the four waves' partials");
 
-// One counting pass of the block select over N moments at once (one
-// histogram each, so the moments share the pass's four barriers): counts
-// digit(k, key) over the keys of moment k with take(k, key), then finds the
-// bin holding the rank[k]-th smallest of them; bin[k], rank[k] (now the
-// rank within that bin) and count[k] (the keys in that bin) come back
-// block-uniform.  act[k] (block-uniform) skips moment k.  Keys are |x| as
-// bit patterns (the order of non-negative floats); digit(k, key) returns the
-// bin's byte offset in the histogram (4 x the bin), so that the address is
-// the digit itself.
-template <int N, int kBins, class Digit, class Take>
-__device__ __forceinline__ void select_pass(const float *const (&x)[N], const bool (&act)[N], Digit digit,
-                                            Take take, uint32_t (&bin)[N], uint32_t (&rank)[N],
-                                            uint32_t (&count)[N], uint32_t (*hist)[kBlock],
-                                            uint32_t (*scratch)[kSelRow]) {
-    static_assert(kBins % kThreads == 0 && kBins <= kBlock, "bins per thread");
-    constexpr int per = kBins / kThreads;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        if (!act[k]) continue;
-        // this thread's `per` adjacent bins, in 16-byte stores where they fit
-        if constexpr (per % 4 == 0) {
-            uint4 *h4 = reinterpret_cast<uint4 *>(&hist[k][tid * per]);
-#pragma unroll
-            for (int i = 0; i < per / 4; ++i) h4[i] = uint4{0u, 0u, 0u, 0u};
-        } else {
-#pragma unroll
-            for (int i = 0; i < per; ++i) hist[k][tid * per + i] = 0u;
-        }
-    }
-    __syncthreads();
+// Histogram counting of one pass: moment k's keys with take(k, key) add 1 at
+// byte offset digit(k, key) of hist[k] (LDS atomics; the caller's barrier
+// completes them).  Keys are |x| as bit patterns (the order of non-negative
+// floats).
+template <int N, int kRow, class Digit, class Take>
+__device__ __forceinline__ void hist_count(const float *const (&x)[N], const bool (&act)[N], Digit digit,
+                                           Take take, uint32_t (*hist)[kRow]) {
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         if (!act[k]) continue;
 #pragma unroll
         for (int i = 0; i < kItems; ++i) {
             const uint32_t key = __float_as_uint(x[k][i]) & 0x7FFFFFFFu;
-            if (take(k, key)) atomicAdd(reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(hist[k]) + digit(k, key)), 1u);
+            if (take(k, key))
+                atomicAdd(reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(hist[k]) + digit(k, key)), 1u);
         }
     }
-    __syncthreads();
-    uint32_t mine[N], incl[N];
+}
+
+// One wave finds the bin of a 2048-bin histogram holding the rank-th
+// smallest counted key: lane L sums bins [32 L, 32 L + 32), a wave prefix
+// sum and a ballot find the lane whose range holds the rank, then lanes
+// 0..31 take one bin each of that range and a second prefix sum and ballot
+// find the bin.  Returns (bin, rank within it, its count), wave-uniform.  If
+// no bin holds the rank (possible only when NaN keys upset the counts) the
+// answer is some bin of the histogram.
+__device__ __forceinline__ uint4 wave_pick_2048(const uint32_t *hist, uint32_t rank) {
+    const int lane = local_tid() & 63;
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + 32 * lane);
+    uint32_t sum = 0u;
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
-        mine[k] = 0u;
-        incl[k] = 0u;
-        if (!act[k]) continue;
-#pragma unroll
-        for (int i = 0; i < per; ++i) mine[k] += hist[k][tid * per + i];
-        incl[k] = wave_inclusive_sum(mine[k]);
-        if (lane == 63) scratch[k][wave] = incl[k];
+    for (int i = 0; i < 8; i += 4) {
+        // four 16-byte reads in flight at a time (all eight would hold 32
+        // registers at once)
+        const uint4 q0 = h4[i], q1 = h4[i + 1], q2 = h4[i + 2], q3 = h4[i + 3];
+        sum += (q0.x + q0.y + q0.z + q0.w) + (q1.x + q1.y + q1.z + q1.w) + (q2.x + q2.y + q2.z + q2.w) +
+               (q3.x + q3.y + q3.z + q3.w);
+        asm volatile("" ::: "memory");
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        if (!act[k]) continue;
-        // the earlier waves' totals, all four read at once (wave-uniform selects)
-        const uint4 part = *reinterpret_cast<const uint4 *>(&scratch[k][0]);
-        incl[k] += (wave > 0 ? part.x : 0u) + (wave > 1 ? part.y : 0u) + (wave > 2 ? part.z : 0u);
-        const uint32_t excl = incl[k] - mine[k];
-        if (excl <= rank[k] && rank[k] < incl[k]) {
-            // the bin is among this thread's: read them at once and take the
-            // first whose running count passes the rank (no chain of
-            // dependent LDS reads while the other waves wait)
-            uint32_t hb[per];
-#pragma unroll
-            for (int i = 0; i < per; ++i) hb[i] = hist[k][tid * per + i];
-            uint32_t cum = excl, b = (uint32_t)(tid * per);
-            bool found = false;
-#pragma unroll
-            for (int i = 0; i < per; ++i) {
-                const bool step = !found && cum + hb[i] <= rank[k];
-                cum = step ? cum + hb[i] : cum;
-                b += step ? 1u : 0u;
-                found = found || !step;
-            }
-            *reinterpret_cast<uint4 *>(&scratch[k][kWaves]) = uint4{b, rank[k] - cum, hist[k][b], 0u};
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        if (!act[k]) continue;
-        // block-uniform: scalar registers (as vector values they crowd the
-        // kernel's vector registers into spills)
-        const uint4 res = *reinterpret_cast<const uint4 *>(&scratch[k][kWaves]);
-        bin[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.x);
-        rank[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.y);
-        count[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.z);
-    }
+    const uint32_t incl = wave_inclusive_sum(sum);
+    const uint64_t hit = __ballot(incl - sum <= rank && rank < incl);
+    const int L = hit ? __builtin_ctzll(hit) : 0;
+    const uint32_t below = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);
+    const uint32_t hb = lane < 32 ? hist[32 * L + lane] : 0u;
+    const uint32_t incl2 = below + wave_inclusive_sum(hb);
+    const uint64_t hit2 = __ballot(lane < 32 && incl2 - hb <= rank && rank < incl2);
+    const int j = hit2 ? __builtin_ctzll(hit2) : 0;
+    const uint32_t below2 = (uint32_t)__builtin_amdgcn_readlane((int)(incl2 - hb), j);
+    const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)hb, j);
+    return uint4{(uint32_t)(32 * L + j), rank - below2, cnt, 0u};
+}
+
+// The same for a 256-bin histogram, by every wave for itself (no barrier
+// after it): lane L holds bins [4 L, 4 L + 4); the four bins of the lane
+// whose range holds the rank are settled in scalar registers.
+__device__ __forceinline__ void wave_pick_256(const uint32_t *hist, uint32_t rank, uint32_t &bin, uint32_t &rank_in,
+                                              uint32_t &count) {
+    const int lane = local_tid() & 63;
+    const uint4 q = reinterpret_cast<const uint4 *>(hist)[lane];
+    const uint32_t sum = q.x + q.y + q.z + q.w;
+    const uint32_t incl = wave_inclusive_sum(sum);
+    const uint64_t hit = __ballot(incl - sum <= rank && rank < incl);
+    const int L = hit ? __builtin_ctzll(hit) : 0;
+    uint32_t r = rank - (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);
+    const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)q.x, L);
+    const uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane((int)q.y, L);
+    const uint32_t b2 = (uint32_t)__builtin_amdgcn_readlane((int)q.z, L);
+    const uint32_t b3 = (uint32_t)__builtin_amdgcn_readlane((int)q.w, L);
+    uint32_t b = 4u * (uint32_t)L, c = b0;
+    if (r >= b0) { r -= b0; ++b; c = b1;
+        if (r >= b1) { r -= b1; ++b; c = b2;
+            if (r >= b2) { r -= b2; ++b; c = b3; } } }
+    bin = b;
+    rank_in = r;
+    count = c;
 }
 
 // The answer when it is the largest or the smallest key of its bin (the
@@ -292,7 +295,7 @@ __device__ __forceinline__ void block_end_pick(const float *const (&x)[N], const
                                                const uint32_t (&lo)[N], const uint32_t (&width)[N],
                                                const uint32_t (&rank)[N], const uint32_t (&count)[N],
                                                uint32_t (&out)[N], uint32_t (*scratch)[kSelRow]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = local_tid(), lane = t & 63, wave = t >> 6;
     uint32_t sx[N], c[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
@@ -323,7 +326,7 @@ __device__ __forceinline__ void block_end_pick(const float *const (&x)[N], const
 // DPP wave sum and one barrier, the rounds alternating between two LDS slot
 // rows so that one barrier per round orders them).
 __device__ __forceinline__ uint32_t block_bisect(const float *x, uint32_t rank, uint32_t (*slots)[kWaves]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = local_tid(), lane = t & 63, wave = t >> 6;
     uint32_t lo = 0u;
 #pragma unroll 1
     for (int bit = 30; bit >= 0; --bit) {
@@ -342,32 +345,58 @@ __device__ __forceinline__ uint32_t block_bisect(const float *x, uint32_t rank, 
     return lo;
 }
 
+// Before the block maximum's barrier: the select's histograms start at zero
+// (that barrier orders these stores before the select's counting).
+template <int N>
+__device__ __forceinline__ void select_clear(const bool (&act)[N], uint32_t (*hist)[kBlock],
+                                             uint32_t (*fine)[kFineBins]) {
+    const int tid = local_tid();
+    static_assert(kBlock == 2 * 4 * kThreads && kFineBins == 4 * 64, "clear in 16-byte stores");
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        if (!act[k]) continue;
+        uint4 *h4 = reinterpret_cast<uint4 *>(hist[k]);
+        h4[tid] = zero4();
+        h4[tid + kThreads] = zero4();
+        if (tid < 64) reinterpret_cast<uint4 *>(fine[k])[tid] = zero4();
+    }
+}
+
 // rank-th smallest (0-based) of the block's 2048 keys (8 per thread) of each
-// of N moments, by LDS radix select.  top[k] is moment k's largest key (the
-// block maximum, known before the select), E its exponent field.
+// of N moments, by LDS radix select (select_clear ran before the block
+// maximum's barrier).  top[k] is moment k's largest key (the block maximum),
+// E its exponent field.
 //   coarse pass: the digit is the key's binade below E (0..14) and its top 7
 //           mantissa bits: bin = (key >> 16) - ((E - 15) << 7), i.e. 128 +
 //           128 (14 - d) + mantissa for a key d binades below E, clamped to
 //           [127, 2047], so that every key 15 or more binades below E lands
 //           in bin 127 (four instructions per key: extract, subtract,
-//           clamp, and the shift to a byte offset).  Moments cluster in a few binades under the block maximum, so 128
-//           bins per binade keep few keys per bin and few lanes of a wave's
-//           atomic add meet on one LDS word (a digit of the top 11 key bits
-//           puts ~80 keys of the densest binade in one of its 8 bins).  A bin
-//           >= 128 fixes the key's bits 30..16;
-//   fine passes: bits 15..8, then 7..0, of the keys in that bin, 256 bins.
+//           clamp, and the shift to a byte offset).  Moments cluster in a
+//           few binades under the block maximum, so 128 bins per binade keep
+//           few keys per bin and few lanes of a wave's atomic add meet on one
+//           LDS word (a digit of the top 11 key bits puts ~80 keys of the
+//           densest binade in one of its 8 bins).  A bin >= 128 fixes the
+//           key's bits 30..16.  After the counting barrier wave k alone scans
+//           moment k's histogram (wave_pick_2048) and publishes the bin; a
+//           second barrier hands it to every wave;
+//   fine passes: bits 15..8, then 7..0, of the keys in that bin, 256 bins,
+//           each wave scanning the small histogram for itself (one barrier
+//           per pass).
 // After the coarse pass and after the first fine pass, a moment whose answer
-// is the largest or the smallest key of its bin (rank count - 1 or 0: a
-// bin holding one or two keys, or the end of a longer one) skips the rest
-// and takes it by block_end_pick; the moments still undecided run the next
-// pass.  When the answer lies in bin 127 (15 binades or more below the
-// maximum: zeros and tiny values, e.g. a low percentile of a block with
-// exact zeros), that moment's statistic comes from block_bisect over all its
-// keys instead.
+// is the largest or the smallest key of its bin (rank count - 1 or 0: a bin
+// holding one or two keys, or the end of a longer one) skips the rest and
+// takes it by block_end_pick; the moments still undecided run the next pass
+// (the first fine pass in its own pre-cleared histogram; the rare second in
+// the coarse histogram's first 256 words, cleared behind a barrier).  When
+// the answer lies in bin 127 (15 binades or more below the maximum: zeros and
+// tiny values, e.g. a low percentile of a block with exact zeros), that
+// moment's statistic comes from block_bisect over all its keys instead.
 template <int N>
 __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N], const uint32_t (&top)[N],
                                uint32_t rank0, uint32_t (&out)[N], uint32_t (*hist)[kBlock],
-                               uint32_t (*scratch)[kSelRow]) {
+                               uint32_t (*fine)[kFineBins], uint32_t (*scratch)[kSelRow]) {
+    static_assert(N <= kWaves, "one scanning wave per moment");
+    const int wave = local_tid() >> 6;
     // stage of each moment (block-uniform): 0 done or inactive, 1 bisection,
     // 2 end pick, 3 next counting pass
     int32_t base[N];
@@ -375,20 +404,32 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         base[k] = ((int32_t)(top[k] >> 23) - 15) * 128;
-        rank[k] = rank0;
-        bin[k] = 0u;
-        count[k] = 0u;
         out[k] = 0u;
     }
-    select_pass<N, kBlock>(
+    hist_count<N, kBlock>(
         x, act,
         [&](int k, uint32_t key) {
             return (uint32_t)min(max((int32_t)(key >> 16) - base[k], 127), kBlock - 1) * 4u;
         },
-        [](int, uint32_t) { return true; }, bin, rank, count, hist, scratch);
+        [](int, uint32_t) { return true; }, hist);
+    __syncthreads();
+    bool scans = false;  // wave-uniform: this wave scans moment `wave`
+#pragma unroll
+    for (int k = 0; k < N; ++k) scans = scans || (wave == k && act[k]);
+    if (scans) {
+        const uint4 res = wave_pick_2048(hist[wave], rank0);
+        if ((local_tid() & 63) == 0) *reinterpret_cast<uint4 *>(&scratch[wave][kWaves]) = res;
+    }
+    __syncthreads();
     bool more[N], any = false;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
+        // block-uniform: scalar registers (as vector values they crowd the
+        // kernel's vector registers into spills)
+        const uint4 res = *reinterpret_cast<const uint4 *>(&scratch[k][kWaves]);
+        bin[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.x);
+        rank[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.y);
+        count[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)res.z);
         pfx[k] = (uint32_t)((int32_t)bin[k] + base[k]) << 16;  // bits 30..16 of the bin's keys
         mask[k] = 0x7FFF0000u;
         stage[k] = !act[k] ? 0u : bin[k] == 127u ? 1u : (rank[k] == 0u || rank[k] + 1u == count[k]) ? 2u : 3u;
@@ -396,13 +437,15 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
         any = any || more[k];
     }
     if (any) {  // block-uniform
-        select_pass<N, 256>(
+        hist_count<N, kFineBins>(
             x, more, [](int, uint32_t key) { return (key >> 6) & (255u << 2); },
-            [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; }, bin, rank, count, hist, scratch);
+            [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; }, fine);
+        __syncthreads();
         any = false;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             if (more[k]) {
+                wave_pick_256(fine[k], rank[k], bin[k], rank[k], count[k]);
                 pfx[k] |= bin[k] << 8;  // bits 30..8
                 mask[k] = 0x7FFFFF00u;
                 stage[k] = (rank[k] == 0u || rank[k] + 1u == count[k]) ? 2u : 3u;
@@ -410,17 +453,27 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
             more[k] = stage[k] == 3u;
             any = any || more[k];
         }
-        if (any) {
-            select_pass<N, 256>(
-                x, more, [](int, uint32_t key) { return (key << 2) & (255u << 2); },
-                [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; }, bin, rank, count, hist, scratch);
+        if (any) {  // the coarse histograms were last read before the publishing barrier
 #pragma unroll
             for (int k = 0; k < N; ++k)
-                if (more[k]) out[k] = pfx[k] | bin[k];
+                if (more[k] && local_tid() < kFineBins / 4)
+                    reinterpret_cast<uint4 *>(hist[k])[local_tid()] = zero4();
+            __syncthreads();
+            hist_count<N, kBlock>(
+                x, more, [](int, uint32_t key) { return (key << 2) & (255u << 2); },
+                [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; }, hist);
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < N; ++k) {
+                if (more[k]) {
+                    wave_pick_256(hist[k], rank[k], bin[k], rank[k], count[k]);
+                    out[k] = pfx[k] | bin[k];
+                }
+            }
         }
     }
-    // the last pass's final barrier ordered every read of the partial-sum
-    // words before the end pick's writes to them
+    // the end pick's partial maxima use words of the scratch rows that no
+    // pass reads
     bool end[N];
     any = false;
 #pragma unroll
@@ -434,7 +487,8 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
         for (int k = 0; k < N; ++k) width[k] = (~mask[k] & 0x7FFFFFFFu) + 1u;  // keys of one bin
         block_end_pick<N>(x, end, pfx, width, rank, count, out, scratch);
     }
-    // the histograms are free after the last pass's barrier
+    // a moment left for the bisection has its own coarse histogram, which no
+    // wave reads after the publishing barrier
 #pragma unroll
     for (int k = 0; k < N; ++k)
         if (stage[k] == 1u) out[k] = block_bisect(x[k], rank0, reinterpret_cast<uint32_t (*)[kWaves]>(hist[k]));
@@ -695,7 +749,7 @@ struct BlockRegs {
 template <int kStore, bool kGradBf16, bool kAms, bool kFull>
 __device__ __forceinline__ void load_data(const StepArgs &a, const BlockCtx &c,
                                           BlockRegs<kStore, kGradBf16, kAms> &r) {
-    const int tid = threadIdx.x;
+    const int tid = kFull ? (int)threadIdx.x : local_tid();  // the ragged path: see local_tid
     r.Am = kStore == kStoreQ8 ? a.m_scale[c.slot] : 0.0f;
     r.Av = kStore != kStoreBf16 ? a.v_scale[c.slot] : 0.0f;
     r.Aw = kAms && kStore != kStoreBf16 ? a.w_scale[c.slot] : 0.0f;
@@ -795,8 +849,9 @@ struct SelectLds<kPctTop, kN> {  // wave lists of the walks (m, v, AMSGrad maxim
     uint32_t res[3];  // merged statistic of each moment
 };
 template <int kN>
-struct SelectLds<kPctRadix, kN> {  // one histogram + scan scratch per moment
-    alignas(16) uint32_t h[kN][kBlock];  // 16-byte aligned rows: cleared in 16-byte stores
+struct SelectLds<kPctRadix, kN> {  // histograms + scratch row per moment
+    alignas(16) uint32_t h[kN][kBlock];      // coarse pass (16-byte aligned rows: cleared in 16-byte stores)
+    alignas(16) uint32_t f[kN][kFineBins];   // first fine pass
     alignas(16) uint32_t s[kN][kSelRow];
 };
 
@@ -1011,6 +1066,15 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         }
         static_assert(kWaves > 1, "block_max's barrier orders the wave lists");
         if (need_m || need_v || need_w) {
+            if constexpr (kPct == kPctRadix) {
+                if constexpr (kAms) {
+                    const bool act[3] = {need_m, need_v, need_w};
+                    select_clear<3>(act, sel.h, sel.f);
+                } else {
+                    const bool act[2] = {need_m, need_v};
+                    select_clear<2>(act, sel.h, sel.f);
+                }
+            }
             if constexpr (kAms) {
                 float x[3] = {mmax, vmax, wmax};
                 block_max<3>(x, lds.red);
@@ -1047,7 +1111,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                     const bool act[3] = {need_m, need_v, need_w};
                     const uint32_t top[3] = {__float_as_uint(mmax), __float_as_uint(vmax), __float_as_uint(wmax)};
                     uint32_t res[3];
-                    block_select_n<3>(xs, act, top, rank, res, sel.h, sel.s);
+                    block_select_n<3>(xs, act, top, rank, res, sel.h, sel.f, sel.s);
                     st[0] = __uint_as_float(res[0]);
                     st[1] = __uint_as_float(res[1]);
                     st[2] = __uint_as_float(res[2]);
@@ -1056,7 +1120,7 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
                     const bool act[2] = {need_m, need_v};
                     const uint32_t top[2] = {__float_as_uint(mmax), __float_as_uint(vmax)};
                     uint32_t res[2];
-                    block_select_n<2>(xs, act, top, rank, res, sel.h, sel.s);
+                    block_select_n<2>(xs, act, top, rank, res, sel.h, sel.f, sel.s);
                     st[0] = __uint_as_float(res[0]);
                     st[1] = __uint_as_float(res[1]);
                 }
@@ -1166,10 +1230,11 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 // with no memory spills (checked per variant; the stochastic-rounding
 // AMSGrad variants would spill and keep the compiler's choice).  8-bit
 // ViT-Base set at percentile 99.0: 317 Gparams/s at 8 waves against 309 at
-// 7.
-constexpr int select_waves(int store, bool sr, int pct, bool ams) {
+// 7.  The static-scale 8-bit variants carry the kept scales besides and take
+// one wave fewer (at 8 they spill a register to memory).
+constexpr int select_waves(int store, bool sr, int pct, bool ams, bool stat) {
     if (pct != 2 || (sr && ams)) return 1;
-    if (store == kStoreQ8) return !sr && !ams ? 8 : (sr ? 7 : 6);
+    if (store == kStoreQ8) return (!sr && !ams ? 8 : (sr ? 7 : 6)) - (stat ? 1 : 0);
     return !sr && !ams ? 7 : 6;
 }
 
@@ -1177,7 +1242,7 @@ constexpr int select_waves(int store, bool sr, int pct, bool ams) {
 // grid size).  Descriptors [0, n_full) are full blocks, whose path has no
 // tail checks; the rest are the tensors' ragged last blocks.
 template <int kStore, bool kGradBf16, bool kSR, int kPct, bool kStatic, bool kAms>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(select_waves(kStore, kSR, kPct, kAms))))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(select_waves(kStore, kSR, kPct, kAms, kStatic))))
 adam_step_kernel(StepArgs a) {
     __shared__ BlockLds lds;
     __shared__ SelectLds<kPct, kAms ? 3 : 2> sel;
