@@ -358,7 +358,7 @@ __device__ __forceinline__ void select_clear(const bool (&act)[N], uint32_t (*hi
         uint4 *h4 = reinterpret_cast<uint4 *>(hist[k]);
         h4[tid] = zero4();
         h4[tid + kThreads] = zero4();
-        if (tid < 64) reinterpret_cast<uint4 *>(fine[k])[tid] = zero4();
+        if (N <= 2 && tid < 64) reinterpret_cast<uint4 *>(fine[k])[tid] = zero4();
     }
 }
 
@@ -386,8 +386,9 @@ __device__ __forceinline__ void select_clear(const bool (&act)[N], uint32_t (*hi
 // is the largest or the smallest key of its bin (rank count - 1 or 0: a bin
 // holding one or two keys, or the end of a longer one) skips the rest and
 // takes it by block_end_pick; the moments still undecided run the next pass
-// (the first fine pass in its own pre-cleared histogram; the rare second in
-// the coarse histogram's first 256 words, cleared behind a barrier).  When
+// (the first fine pass in its own pre-cleared histogram, or with three
+// moments in the coarse histogram's words 0..255; the rare second in its
+// words 256..511; both of the latter cleared behind a barrier).  When
 // the answer lies in bin 127 (15 binades or more below the maximum: zeros and
 // tiny values, e.g. a low percentile of a block with exact zeros), that
 // moment's statistic comes from block_bisect over all its keys instead.
@@ -437,15 +438,33 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
         any = any || more[k];
     }
     if (any) {  // block-uniform
-        hist_count<N, kFineBins>(
-            x, more, [](int, uint32_t key) { return (key >> 6) & (255u << 2); },
-            [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; }, fine);
+        // N = 3: in the coarse histogram's first 256 words, free after the
+        // publishing barrier, cleared behind one more barrier
+        uint32_t *fh[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            if constexpr (N <= 2) fh[k] = fine[k];
+            else fh[k] = hist[k];
+        }
+        if constexpr (N > 2) {
+#pragma unroll
+            for (int k = 0; k < N; ++k)
+                if (more[k] && local_tid() < kFineBins / 4)
+                    reinterpret_cast<uint4 *>(hist[k])[local_tid()] = zero4();
+            __syncthreads();
+        }
+        const auto fine_digit = [](int, uint32_t key) { return (key >> 6) & (255u << 2); };
+        const auto fine_take = [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; };
+        if constexpr (N <= 2)
+            hist_count<N, kFineBins>(x, more, fine_digit, fine_take, fine);
+        else
+            hist_count<N, kBlock>(x, more, fine_digit, fine_take, hist);
         __syncthreads();
         any = false;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             if (more[k]) {
-                wave_pick_256(fine[k], rank[k], bin[k], rank[k], count[k]);
+                wave_pick_256(fh[k], rank[k], bin[k], rank[k], count[k]);
                 pfx[k] |= bin[k] << 8;  // bits 30..8
                 mask[k] = 0x7FFFFF00u;
                 stage[k] = (rank[k] == 0u || rank[k] + 1u == count[k]) ? 2u : 3u;
@@ -453,20 +472,24 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
             more[k] = stage[k] == 3u;
             any = any || more[k];
         }
-        if (any) {  // the coarse histograms were last read before the publishing barrier
+        if (any) {  // block-uniform
+            // words 256..511 of the coarse histogram: no wave reads them after
+            // the publishing barrier (the first fine pass of three moments
+            // uses words 0..255, which slower waves may still be scanning)
 #pragma unroll
             for (int k = 0; k < N; ++k)
                 if (more[k] && local_tid() < kFineBins / 4)
-                    reinterpret_cast<uint4 *>(hist[k])[local_tid()] = zero4();
+                    reinterpret_cast<uint4 *>(hist[k] + kFineBins)[local_tid()] = zero4();
             __syncthreads();
             hist_count<N, kBlock>(
                 x, more, [](int, uint32_t key) { return (key << 2) & (255u << 2); },
-                [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; }, hist);
+                [&](int k, uint32_t key) { return (key & mask[k]) == pfx[k]; },
+                reinterpret_cast<uint32_t (*)[kBlock]>(hist[0] + kFineBins));
             __syncthreads();
 #pragma unroll
             for (int k = 0; k < N; ++k) {
                 if (more[k]) {
-                    wave_pick_256(hist[k], rank[k], bin[k], rank[k], count[k]);
+                    wave_pick_256(hist[k] + kFineBins, rank[k], bin[k], rank[k], count[k]);
                     out[k] = pfx[k] | bin[k];
                 }
             }
@@ -851,7 +874,10 @@ struct SelectLds<kPctTop, kN> {  // wave lists of the walks (m, v, AMSGrad maxim
 template <int kN>
 struct SelectLds<kPctRadix, kN> {  // histograms + scratch row per moment
     alignas(16) uint32_t h[kN][kBlock];      // coarse pass (16-byte aligned rows: cleared in 16-byte stores)
-    alignas(16) uint32_t f[kN][kFineBins];   // first fine pass
+    // first fine pass; with three moments it shares the coarse histograms
+    // instead (27 KiB of LDS per workgroup would leave room for 5 per CU, 24
+    // KiB leaves room for the 6 their registers allow)
+    alignas(16) uint32_t f[kN <= 2 ? kN : 1][kFineBins];
     alignas(16) uint32_t s[kN][kSelRow];
 };
 

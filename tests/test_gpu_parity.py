@@ -246,6 +246,61 @@ def test_radix_select_far_below_the_maximum(pct, storage, sr, ams):
     st.destroy()
 
 
+def _stage_grads(seed, numels, t):
+    """Gradients that send the radix select down each of its paths, per
+    block: keys a few hundred ulps apart with repeats (the answer's bin needs
+    both fine passes), values spread over three decades (bins of one or two
+    keys: the end pick after the coarse or the first fine pass), two thirds
+    exact zeros (bisection at low percentiles), plain normal."""
+    rng = np.random.default_rng([seed, t])
+    out = []
+    for n in numels:
+        g = rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)
+        kinds = rng.integers(0, 4, (n + 2047) // 2048)
+        for b, k in enumerate(kinds):
+            blk = g[2048 * b:2048 * (b + 1)]
+            if k == 0:
+                near = np.float32(1e-3).view(np.uint32) + rng.integers(0, 600, blk.size).astype(np.uint32)
+                blk[:] = near.view(np.float32) * np.where(rng.random(blk.size) < 0.5, -1, 1).astype(np.float32)
+            elif k == 1:
+                blk *= (np.float32(10.0) ** rng.uniform(-3, 0, blk.size)).astype(np.float32)
+            elif k == 2:
+                blk[:blk.size * 2 // 3] = 0.0
+        out.append(g)
+    return out
+
+
+@pytest.mark.parametrize("pct", [10.0, 50.0, 99.0])
+@pytest.mark.parametrize("storage,sr,ams", [("q8", False, False), ("q8", False, True), ("q8", True, False),
+                                            ("q8", True, True), ("q8_v_only", False, True)])
+def test_radix_select_every_stage(pct, storage, sr, ams):
+    # beta1 = beta2 = 0: m = g and v = fl(g^2) exactly, so the constructed
+    # gradients fix the keys of the select (a host model of its decisions
+    # puts blocks of these gradients on the end pick after the coarse pass
+    # and after the first fine pass, on both fine passes, and on the
+    # bisection); two moments, and three with AMSGrad
+    numels = RAGGED + [2048 * 8]
+    log(f"radix select, every stage: percentile {pct} {storage} sr={sr} amsgrad={ams}")
+    params = workloads.host_params(31, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, storage, "f32", amsgrad=ams)
+    ost = oracle.OracleState(numels, storage, amsgrad=ams)
+    stats = Stats()
+    hp = dict(HP, beta1=0.0, beta2=0.0, stochastic=sr, percentile=pct, seed=37)
+    for t in range(1, 4):
+        grads = _stage_grads(31, numels, t)
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t} tensor {k}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, sr, stats, f"t={t}")
+    log(f"  {stats}")
+    st.destroy()
+
+
 def _one_lane_top_grads(seed, numels, t):
     # in every full block one lane of one wave (lane 5 of wave b mod 4: block
     # elements 256w + 20 .. + 23 and 1024 + 256w + 20 .. + 23) holds the eight
