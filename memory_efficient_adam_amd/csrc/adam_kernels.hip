@@ -117,22 +117,6 @@ constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr3 = 0x113, kRowShr4 = 0
 constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
-__device__ __forceinline__ float fmax_dpp_row(float x) {
-    x = fmaxf(x, __uint_as_float(dpp<kQuadPerm1032>(__float_as_uint(x))));
-    x = fmaxf(x, __uint_as_float(dpp<kQuadPerm2301>(__float_as_uint(x))));
-    x = fmaxf(x, __uint_as_float(dpp<kRowRor4>(__float_as_uint(x))));
-    x = fmaxf(x, __uint_as_float(dpp<kRowRor8>(__float_as_uint(x))));
-    return x;  // every lane holds its row's max
-}
-
-// Max over the wave of non-negative values, as a wave-uniform value.
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmax_dpp_row(x);
-    x = fmaxf(x, __uint_as_float(dpp<kRowBcast15, 0xA>(__float_as_uint(x))));
-    x = fmaxf(x, __uint_as_float(dpp<kRowBcast31, 0xC>(__float_as_uint(x))));
-    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), 63));
-}
-
 // Max over the wave of unsigned values, as a wave-uniform value.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
     x = max(x, dpp<kQuadPerm1032>(x));
@@ -173,23 +157,27 @@ __device__ __forceinline__ uint4 zero4() {
     return uint4{z, z, z, z};
 }
 
-// Block-wide max of N non-negative values per thread (one barrier).
+// Block-wide max of N non-negative values per thread (one barrier).  The
+// values are never NaN (each is an fmaxf over |m|, v or the AMSGrad maximum
+// from 0, which drops NaN), so the order of their bit patterns, with the sign
+// bit cleared (-0 -> +0), is the float order: one DPP integer max per step
+// (a float max would add a quieting max to each DPP move).
 template <int N>
 __device__ __forceinline__ void block_max(float (&x)[N], float (*red)[kWaves]) {
     const int t = local_tid(), lane = t & 63, wave = t >> 6;
+    uint32_t u[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) x[i] = wave_max(x[i]);
-    if (kWaves == 1) return;
+    for (int i = 0; i < N; ++i) u[i] = wave_max_u32(__float_as_uint(x[i]) & 0x7FFFFFFFu);
+    static_assert(kWaves == 4, "four partial maxima");
     if (lane == 0) {
 #pragma unroll
-        for (int i = 0; i < N; ++i) red[i][wave] = x[i];
+        for (int i = 0; i < N; ++i) red[i][wave] = __uint_as_float(u[i]);
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        x[i] = red[i][0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) x[i] = fmaxf(x[i], red[i][w]);
+        const uint4 q = *reinterpret_cast<const uint4 *>(red[i]);
+        x[i] = __uint_as_float(max(max(q.x, q.y), max(q.z, q.w)));
     }
 }
 
@@ -855,7 +843,7 @@ __device__ __forceinline__ void load_data(const StepArgs &a, const BlockCtx &c,
 
 // LDS of one block's max reduction (m, v and the AMSGrad maximum).
 struct BlockLds {
-    float red[3][kWaves];
+    alignas(16) float red[3][kWaves];  // rows read as one 16-byte word
 };
 
 // Block statistic of a step: the block maximum, or the percentile taken by
