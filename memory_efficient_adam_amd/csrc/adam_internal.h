@@ -54,6 +54,7 @@ struct StepArgs {
     uint32_t l2;     // 1: Adam with L2-coupled decay (g += wd*p)
     uint32_t fast_ok;  // 1: eps in [2^-40, 2^20], so the short exact sqrt/divide may apply
     double pfrac;    // percentile / 100 (percentile statistic)
+    uint32_t rank_full;  // floor(pfrac * 2047): the percentile's rank in a full block
     uint32_t seed_lo, seed_hi, t_lo, t_hi;
     uint32_t n_full;   // descriptors [0, n_full) are full blocks
     uint32_t n_all;    // descriptors [n_full, n_all) are ragged last blocks

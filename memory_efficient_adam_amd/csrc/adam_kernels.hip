@@ -1069,7 +1069,9 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
         // adds zeros below the n values), i.e. the need-th largest
         uint32_t rank = 0, need = 0;
         if constexpr (kPct != kPctNone) {
-            rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
+            // (full blocks: the same double arithmetic, done once on the host)
+            if constexpr (kFull) rank = a.rank_full;
+            else rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
             need = kBlock - rank;  // in [1, kWalkNeed] for kPctTop (walk_covers)
         }
         if constexpr (kPct == kPctTop) {  // wave walks; the barrier in block_max publishes their lists

@@ -252,6 +252,7 @@ void fill_scalars(StepArgs &a, const adam_hparams *hp) {
     a.l2 = decoupled ? 0u : 1u;
     a.fast_ok = (hp->eps >= 0x1p-40f && hp->eps <= 0x1p20f) ? 1u : 0u;
     a.pfrac = (double)hp->percentile / 100.0;
+    a.rank_full = (uint32_t)floor(a.pfrac * (double)(kBlock - 1));  // the kernel's own arithmetic
     a.seed_lo = (uint32_t)hp->seed;
     a.seed_hi = (uint32_t)(hp->seed >> 32);
     a.t_lo = (uint32_t)(uint64_t)hp->t;
