@@ -222,8 +222,10 @@ __device__ __forceinline__ uint4 wave_pick_2048(const uint32_t *hist, uint32_t r
 #pragma unroll
     for (int i = 0; i < 8; i += 4) {
         // four 16-byte reads in flight at a time (all eight would hold 32
-        // registers at once)
-        const uint4 q0 = h4[i], q1 = h4[i + 1], q2 = h4[i + 2], q3 = h4[i + 3];
+        // registers at once); lane L starts at its chunk L mod 8, so that the
+        // lanes of one read (128 bytes apart) spread over the LDS banks
+        const uint4 q0 = h4[(i + lane) & 7], q1 = h4[(i + 1 + lane) & 7], q2 = h4[(i + 2 + lane) & 7],
+                    q3 = h4[(i + 3 + lane) & 7];
         sum += (q0.x + q0.y + q0.z + q0.w) + (q1.x + q1.y + q1.z + q1.w) + (q2.x + q2.y + q2.z + q2.w) +
                (q3.x + q3.y + q3.z + q3.w);
         asm volatile("" ::: "memory");
