@@ -360,8 +360,8 @@ __device__ __forceinline__ void select_clear(const bool (&act)[N], uint32_t (*hi
 //           mantissa bits: bin = (key >> 16) - ((E - 15) << 7), i.e. 128 +
 //           128 (14 - d) + mantissa for a key d binades below E, clamped to
 //           [127, 2047], so that every key 15 or more binades below E lands
-//           in bin 127 (four instructions per key: extract, subtract,
-//           clamp, and the shift to a byte offset).  Moments cluster in a
+//           in bin 127 (three instructions per key: extract, one shift-add
+//           to the byte offset, clamp).  Moments cluster in a
 //           few binades under the block maximum, so 128 bins per binade keep
 //           few keys per bin and few lanes of a wave's atomic add meet on one
 //           LDS word (a digit of the top 11 key bits puts ~80 keys of the
@@ -390,17 +390,22 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
     const int wave = local_tid() >> 6;
     // stage of each moment (block-uniform): 0 done or inactive, 1 bisection,
     // 2 end pick, 3 next counting pass
-    int32_t base[N];
+    int32_t base[N], nbase4[N];
     uint32_t rank[N], bin[N], count[N], pfx[N], mask[N], stage[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         base[k] = ((int32_t)(top[k] >> 23) - 15) * 128;
+        nbase4[k] = -4 * base[k];
         out[k] = 0u;
     }
     hist_count<N, kBlock>(
         x, act,
         [&](int k, uint32_t key) {
-            return (uint32_t)min(max((int32_t)(key >> 16) - base[k], 127), kBlock - 1) * 4u;
+            // 4 (key >> 16) - 4 base in one shift-add (left to itself the
+            // compiler subtracts first and shifts after), clamped in bytes
+            int32_t off;
+            asm("v_lshl_add_u32 %0, %1, 2, %2" : "=v"(off) : "v"(__builtin_amdgcn_ubfe(key, 16, 15)), "s"(nbase4[k]));
+            return (uint32_t)min(max(off, 4 * 127), 4 * (kBlock - 1));
         },
         [](int, uint32_t) { return true; }, hist);
     __syncthreads();
