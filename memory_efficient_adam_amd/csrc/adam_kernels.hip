@@ -190,9 +190,10 @@ __device__ __forceinline__ void block_max(float (&x)[N], float (*red)[kWaves]) {
 }
 
 // Per-moment LDS scratch row of the select: [0, kWaves) the waves' partial
-// maxima of the end pick (or bisection counts), [kWaves] the chosen bin,
-// [kWaves + 1] the rank within it, [kWaves + 2] the bin's count; 8 words, so
-// that each half is one 16-byte access.
+// maxima of the end pick, and the coarse pass's result as published by its
+// scanning wave: [kWaves] the chosen bin, [kWaves + 1] the rank within it,
+// [kWaves + 2] the bin's count; 8 words, so that each half is one 16-byte
+// access.
 constexpr int kSelRow = 8;
 constexpr int kFineBins = 256;
 static_assert(kWaves == 4, "a row's first half holds the four waves' partials");
