@@ -571,7 +571,11 @@ __device__ __forceinline__ void wave_top(const float (&x)[kItems], uint32_t need
             C += (uint32_t)__popcll(__ballot(hit));
             key[i] = hit ? 0u : key[i];
         }
-        if (lane == (int)it) { my_val = M; my_cnt = C; }
+        // lane `it` of the list: one v_writelane each (it, M and C are uniform;
+        // the lane select goes through M0, the one scalar source besides the
+        // value that the instruction may read on this architecture)
+        asm("v_writelane_b32 %0, %1, m0" : "+v"(my_val) : "s"(M), "{m0}"(it));
+        asm("v_writelane_b32 %0, %1, m0" : "+v"(my_cnt) : "s"(C), "{m0}"(it));
         acc += C;
         if (acc >= need) break;
     }
@@ -621,7 +625,11 @@ __device__ __forceinline__ bool wave_top_lanes(const float (&x)[kItems], uint32_
         const uint32_t M = wave_max_u32(k0);
         const bool hit = k0 == M;
         const uint32_t C = (uint32_t)__popcll(__ballot(hit));
-        if (lane == (int)it) { my_val = M; my_cnt = C; }
+        // lane `it` of the list: one v_writelane each (it, M and C are uniform;
+        // the lane select goes through M0, the one scalar source besides the
+        // value that the instruction may read on this architecture)
+        asm("v_writelane_b32 %0, %1, m0" : "+v"(my_val) : "s"(M), "{m0}"(it));
+        asm("v_writelane_b32 %0, %1, m0" : "+v"(my_cnt) : "s"(C), "{m0}"(it));
         acc += C;
         if (acc >= need) break;
         k0 = hit ? k1 : k0;
