@@ -315,10 +315,10 @@ def main():
         cfg = dataclasses.replace(cfg, amsgrad=True)
     hp = apply_overrides(cfg, args)
     # counter readings are taken per workload for its own kernel variant (a
-    # percentile run of an 8-bit set has its own record when one was taken)
-    variant_changed = args.static_scales or cfg.amsgrad
-    key = None if variant_changed else cfg.name + ("_nearest" if args.nearest else "") + (
-        "" if args.percentile is None else f"_percentile{args.percentile}")
+    # percentile, nearest-rounding or AMSGrad run of a set has its own record
+    # when one was taken; static scales have none)
+    key = None if args.static_scales else cfg.name + ("_amsgrad" if cfg.amsgrad else "") + (
+        "_nearest" if args.nearest else "") + ("" if args.percentile is None else f"_percentile{args.percentile}")
     rec = time_workload(cfg, hp, args.steps, args.warmup, args.grad_buffers, key)
     out = {
         "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",
