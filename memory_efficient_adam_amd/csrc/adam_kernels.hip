@@ -539,13 +539,15 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
 // `need` keys at or above it in the block, so s >= max_w L_w; at and above
 // that point the union counts every key, and s is in its own wave's list
 // (fewer than `need` keys of the block lie above it).
-// Keys are stored plus one, so 0 marks "dropped" / "empty" and the unsigned
-// max with its identity 0 serves both walks.
+// A key is the value's bit pattern shifted up one place with the low bit set
+// (one v_lshl_or: the sign drops out, the order of magnitudes stays, no key
+// is 0), so 0 marks "dropped" / "empty" and the unsigned max with its
+// identity 0 serves both walks.
 constexpr uint32_t kTopCap = 16;  // entries of a wave's list (the union: one per lane)
 static_assert(kWaves * kTopCap == 64, "one union entry per lane");
 
 
-__device__ __forceinline__ uint32_t top_key(float x) { return (__float_as_uint(x) & 0x7FFFFFFFu) + 1u; }
+__device__ __forceinline__ uint32_t top_key(float x) { return (__float_as_uint(x) << 1) | 1u; }
 
 // top values of |x| over the wave's 512 keys; writes kTopCap (value+1,
 // count) entries at val[wave * kTopCap ...], unused entries (0, 0).
@@ -616,7 +618,9 @@ __device__ __forceinline__ bool wave_top_lanes(const float (&x)[kItems], uint32_
 #pragma unroll
     for (int i = 2; i < kItems; ++i) {
         const uint32_t y = top_key(x[i]);
-        k1 = max(k1, min(k0, y));
+        // with k0 >= k1 the second largest of (k0, k1, y) is their median:
+        // one v_med3 in place of a min and a max
+        asm("v_med3_u32 %0, %1, %2, %3" : "=v"(k1) : "v"(k0), "v"(k1), "v"(y));
         k0 = max(k0, y);
     }
     uint32_t my_val = 0u, my_cnt = 0u, acc = 0u;
@@ -649,32 +653,35 @@ __device__ __forceinline__ void wave_top_any(const float (&x)[kItems], uint32_t 
 }
 
 // need-th largest key over the union of the wave lists (after a barrier
-// that follows every wave_top), computed by one wave.  Each round
-// consumes at least one entry of count >= 1, and the entries hold at least
-// need counts in total, so the walk stops within 64 rounds.
-__device__ __forceinline__ uint32_t top_merge(const uint32_t *val, const uint32_t *cnt, uint32_t need) {
+// that follows every wave_top), computed by one wave, with the largest key
+// of the union, which is the block maximum (each list starts at its wave's
+// largest key).  Returned as magnitude bit patterns {need-th, maximum}.
+// Each round consumes at least one entry of count >= 1, and the entries hold
+// at least need counts in total, so the walk stops within 64 rounds.
+__device__ __forceinline__ uint2 top_merge(const uint32_t *val, const uint32_t *cnt, uint32_t need) {
     const int lane = threadIdx.x & 63;
     uint32_t v = val[lane];
     const uint32_t n = cnt[lane];
-    uint32_t acc = 0u, M = 1u;
+    const uint32_t top = wave_max_u32(v);  // every list starts at its wave's largest key
+    uint32_t acc = 0u, M = top;
     if (__ballot(n > 1u) == 0) {  // every entry one key (distinct values): a ballot counts a round
         for (int it = 0; it < 64; ++it) {
-            M = wave_max_u32(v);
             const bool hit = v == M;
             acc += (uint32_t)__popcll(__ballot(hit));
             if (acc >= need) break;
             v = hit ? 0u : v;
+            M = wave_max_u32(v);
         }
     } else {
         for (int it = 0; it < 64; ++it) {
-            M = wave_max_u32(v);
             const uint32_t s = wave_inclusive_sum(v == M ? n : 0u);
             acc += (uint32_t)__builtin_amdgcn_readlane((int)s, 63);
             if (acc >= need) break;
             v = v == M ? 0u : v;
+            M = wave_max_u32(v);
         }
     }
-    return M - 1u;
+    return make_uint2(M >> 1, top >> 1);
 }
 
 // ---------------------------------------------------------------- quantizer
@@ -882,6 +889,7 @@ struct SelectLds<kPctTop, kN> {  // wave lists of the walks (m, v, AMSGrad maxim
     uint32_t val[3][kWaves * kTopCap];
     uint32_t cnt[3][kWaves * kTopCap];
     uint32_t res[3];  // merged statistic of each moment
+    uint32_t top[3];  // and its block maximum
 };
 template <int kN>
 struct SelectLds<kPctRadix, kN> {  // histograms + scratch row per moment
@@ -1098,14 +1106,17 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
             else rank = (uint32_t)floor(a.pfrac * (double)(c.n - 1)) + (kBlock - c.n);
             need = kBlock - rank;  // in [1, kWalkNeed] for kPctTop (walk_covers)
         }
-        if constexpr (kPct == kPctTop) {  // wave walks; the barrier in block_max publishes their lists
+        if constexpr (kPct == kPctTop) {  // wave walks; the barrier below publishes their lists
             if (need_m) wave_top_any(mo, need, sel.val[0], sel.cnt[0]);
             if (need_v) wave_top_any(vo, need, sel.val[1], sel.cnt[1]);
             if constexpr (kAms)
                 if (need_w) wave_top_any(wo, need, sel.val[2], sel.cnt[2]);
         }
-        static_assert(kWaves > 1, "block_max's barrier orders the wave lists");
-        if (need_m || need_v || need_w) {
+        if constexpr (kPct == kPctTop) {
+            // the walks' lists hold each wave's largest key: the merge finds
+            // the block maximum too, and this barrier only publishes them
+            if (need_m || need_v || need_w) __syncthreads();
+        } else if (need_m || need_v || need_w) {
             if constexpr (kPct == kPctRadix) {
                 if constexpr (kAms) {
                     const bool act[3] = {need_m, need_v, need_w};
@@ -1133,11 +1144,17 @@ __device__ __forceinline__ void process_block(const StepArgs &a, const BlockCtx 
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
                 if (wave == k && need_k[k]) {
-                    const uint32_t st = top_merge(sel.val[k], sel.cnt[k], need);
-                    if ((threadIdx.x & 63) == 0) sel.res[k] = st;
+                    const uint2 st = top_merge(sel.val[k], sel.cnt[k], need);
+                    if ((threadIdx.x & 63) == 0) {
+                        sel.res[k] = st.x;
+                        sel.top[k] = st.y;
+                    }
                 }
             }
             __syncthreads();
+            mmax = __uint_as_float(sel.top[0]);
+            vmax = __uint_as_float(sel.top[1]);
+            wmax = __uint_as_float(sel.top[2]);
         }
         if constexpr (kPct != kPctNone) {
             float st[3] = {0.0f, 0.0f, 0.0f};
