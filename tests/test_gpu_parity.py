@@ -246,6 +246,56 @@ def test_radix_select_far_below_the_maximum(pct, storage, sr, ams):
     st.destroy()
 
 
+def _sparse_grads(seed, numels, t):
+    """Gradients that are zero except at 0-5 positions per block (the same
+    positions every step, so the moments stay exactly zero elsewhere), with
+    values over eight decades: the need-th largest key is then often 0, and
+    the statistic falls back to the block maximum."""
+    out = []
+    for k, n in enumerate(numels):
+        g = np.zeros(n, np.float32)
+        for b in range((n + 2047) // 2048):
+            lo, hi = 2048 * b, min(n, 2048 * (b + 1))
+            pos_rng = np.random.default_rng([seed, k, b])
+            nz = int(pos_rng.integers(0, 6))
+            pos = lo + pos_rng.choice(hi - lo, min(nz, hi - lo), replace=False)
+            val_rng = np.random.default_rng([seed, k, b, t])
+            g[pos] = (val_rng.standard_normal(pos.size) *
+                      10.0 ** val_rng.uniform(-6, 2, pos.size)).astype(np.float32)
+        out.append(g)
+    return out
+
+
+@pytest.mark.parametrize("pct", [100.0, 99.9, 99.8])
+@pytest.mark.parametrize("storage,sr,ams", [("q8", False, False), ("q8", True, True),
+                                            ("q8_v_only", False, True)])
+def test_percentile_on_sparse_blocks(pct, storage, sr, ams):
+    # blocks with fewer non-zero moments than need: the need-th largest key
+    # is 0, so the scale is the block maximum, which the walks' merge finds
+    # (100 and 99.9: need 1 and 4) or the radix select's max reduction (99.8:
+    # need 6)
+    numels = RAGGED + [2048 * 6]
+    log(f"percentile on sparse blocks: percentile {pct} {storage} sr={sr} amsgrad={ams}")
+    params = workloads.host_params(29, numels)
+    dev_p = [torch.from_numpy(p.copy()).cuda() for p in params]
+    st = ma.adam_state_create(numels, storage, "f32", amsgrad=ams)
+    ost = oracle.OracleState(numels, storage, amsgrad=ams)
+    stats = Stats()
+    hp = dict(HP, stochastic=sr, percentile=pct, seed=31)
+    for t in range(1, 4):
+        grads = _sparse_grads(29, numels, t)
+        ma.adam_step(st, dev_p, to_device_grads(grads, "f32"), t=t, **hp)
+        ost.step(params, grads, t=t, **hp)
+        torch.cuda.synchronize()
+        for k in range(len(numels)):
+            compare_params(dev_p[k].cpu().numpy(), params[k], stats, f"t={t} tensor {k}")
+        got = read_state(st)
+        for nm, want in ost.buffers().items():
+            compare_buffer(nm, got[nm], want, sr, stats, f"t={t}")
+    log(f"  {stats}")
+    st.destroy()
+
+
 def _stage_grads(seed, numels, t):
     """Gradients that send the radix select down each of its paths, per
     block: keys a few hundred ulps apart with repeats (the answer's bin needs
@@ -700,10 +750,12 @@ def test_full_size_sampled_blocks_static_scales():
 
 @pytest.mark.parametrize("name", ["vit_bf16", "vit_q8", "gpt1p3b_q8_sr",
                                   "llama7b_mf32_vq8_pct", "llama7b_shard8_mf32_vq8_pct",
-                                  "vit_q8@99.0", "vit_q8@50.0"])
+                                  "vit_q8@99.0", "vit_q8@50.0", "vit_q8@99.9",
+                                  "gpt1p3b_q8_sr@99.9"])
 def test_full_size_sampled_blocks(name):
-    # name@p: the same set with the percentile-p block statistic (below ~99.27
-    # the radix select serves it), in the benchmark's launch configuration
+    # name@p: the same set with the percentile-p block statistic (the top
+    # walks serve 99.85 and above, the radix select the rest), in the
+    # benchmark's launch configuration
     base, _, pct = name.partition("@")
     cfg = workloads.CONFIGS[base]
     if pct:
