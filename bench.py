@@ -259,6 +259,48 @@ def time_workload(cfg, hp, steps, warmup, grad_buffers, traffic_key=None):
     }
 
 
+PROBE_CAPS = (2, 3, 4, 5, 6, 8)
+
+
+def time_stream_probe(cfg, steps, warmup, caps=PROBE_CAPS):
+    """Times the stream probe over as many full blocks as the workload has
+    blocks: the step's loads and stores without its arithmetic, at each
+    residency cap (workgroups per CU; 8 = uncapped), with HIP events on the
+    launch stream as for the step.  Its bytes per launch are its own (the
+    workload's tail blocks counted as full)."""
+    import torch
+    from memory_efficient_adam_amd import stream_probe as sp
+    n_blocks = sum(-(-k // 2048) for k in cfg.numels())
+    bufs = sp.probe_buffers(n_blocks, cfg.grad_dtype, cfg.storage, cfg.amsgrad)
+    for t in bufs.values():
+        if t is not None:
+            t.zero_()
+    nbytes = sp.adam_stream_probe_bytes(n_blocks, cfg.grad_dtype, cfg.storage, cfg.amsgrad)
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for cap in caps:
+        for _ in range(warmup):
+            sp.adam_stream_probe(bufs, n_blocks, cfg.grad_dtype, cfg.storage, cfg.amsgrad, cap, stream)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            sp.adam_stream_probe(bufs, n_blocks, cfg.grad_dtype, cfg.storage, cfg.amsgrad, cap, stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        gbs = nbytes / (ms / 1e3) / 1e9
+        rates[str(cap)] = {"ms_per_launch": round(ms, 5), "GB/s": round(gbs, 1),
+                           "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del bufs
+    torch.cuda.empty_cache()
+    best = max(rates, key=lambda c: rates[c]["GB/s"])
+    return {"workload": cfg.name, "amsgrad": cfg.amsgrad, "blocks": n_blocks,
+            "bytes_per_launch": nbytes, "steps": steps, "warmup": warmup,
+            "resident_per_cu": rates, "best_cap": int(best), "best": rates[best]}
+
+
 # the 8-bit workloads timed beside the headline (bf16-moment) workload, with
 # the host-oracle sample size for each (blocks) and the grad buffers rotated
 MODES = [("vit_q8", 4096, 4), ("gpt1p3b_q8_sr", 4096, 4), ("llama7b_mf32_vq8_pct", 4096, 2)]
@@ -288,6 +330,9 @@ def main():
                     help="8-bit sets: nearest-even rounding instead of the set's stochastic rounding")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's device copy of 4 GiB (counter calibration run)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="time the stream probe (the step's loads and stores, no arithmetic) "
+                         "on the workload's blocks at several residency caps")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -307,6 +352,17 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}), flush=True)
+        return
+
+    if args.stream_probe:
+        names = [args.config] if args.config else ["vit_bf16"] + [m[0] for m in MODES]
+        out = []
+        for name in names:
+            pcfg = workloads.CONFIGS[name]
+            if args.amsgrad:
+                pcfg = dataclasses.replace(pcfg, amsgrad=True)
+            out.append(time_stream_probe(pcfg, args.steps, args.warmup))
+        print(json.dumps({"stream_probe": out}), flush=True)
         return
 
     headline = args.config is None
