@@ -15,8 +15,9 @@
  * Pattern (the step's): one 256-thread workgroup per 2048-element block;
  * thread t handles elements 4t..4t+3 and 1024+4t..1024+4t+3 of its block;
  * every load and store is non-temporal and as wide as four elements allow
- * (16 bytes of fp32, 8 of bf16, 4 of 8-bit codes); thread 0 reads the
- * block's scales.  With 8-bit moments the block's loads all complete before
+ * (16 bytes of fp32, 8 of bf16, 4 of 8-bit codes); every thread reads the
+ * block's scales (block-uniform addresses) and thread 0 writes them.  With
+ * 8-bit moments the block's loads all complete before
  * a workgroup barrier (the step's block statistic), and the stores follow
  * it.  Workgroups take blocks in the step's XCD order (runs of 16
  * consecutive blocks per XCD) and an LDS reservation caps how many share a
