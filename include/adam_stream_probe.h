@@ -50,10 +50,10 @@ extern "C" {
  *   scales  float[n_scales * n_blocks], moment-major (m, v, then w), with
  *           n_scales = 0 for storage 1, 2 (+1 with amsgrad) for storage 2,
  *           1 (+1 with amsgrad) for storage 3; may be NULL when n_scales = 0
- *   resident_per_cu  at most this many workgroups per CU, 1..8 (8: no cap)
+ *   resident_per_cu  at most this many workgroups per CU, 2..8 (8: no cap)
  * Device buffers are the caller's and must be 16-byte aligned.  Returns 0,
  * -1 (bad argument: storage or grad_bytes out of range, n_blocks 0 or at
- * least 2^24, resident_per_cu outside 1..8, a NULL or misaligned buffer that
+ * least 2^24, resident_per_cu outside 2..8, a NULL or misaligned buffer that
  * the storage needs; nothing is enqueued) or -5 (the launch failed).
  */
 int adam_stream_probe(void *param, const void *grad, void *m, void *v, void *w, float *scales,

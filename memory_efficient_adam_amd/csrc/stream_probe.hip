@@ -169,13 +169,13 @@ extern "C" int adam_stream_probe(void *param, const void *grad, void *m, void *v
                                  int32_t resident_per_cu, void *stream) {
     Layout l;
     if (!layout_of(storage, amsgrad, l) || (grad_bytes != 2 && grad_bytes != 4)) return -1;
-    if (n_blocks == 0 || n_blocks >= (1u << 24) || resident_per_cu < 1 || resident_per_cu > 8) return -1;
+    if (n_blocks == 0 || n_blocks >= (1u << 24) || resident_per_cu < 2 || resident_per_cu > 8) return -1;
     if (!aligned16(param) || !aligned16(grad) || !aligned16(m) || !aligned16(v)) return -1;
     if (l.w && !aligned16(w)) return -1;
     if (l.s && !aligned16(scales)) return -1;
     const ProbeArgs a{static_cast<float *>(param), grad, m, v, w, scales, n_blocks};
     // LDS the kernel does not use, reserved so that at most resident_per_cu
-    // workgroups fit on a CU
+    // workgroups fit on a CU (at 2: 54.6 KiB of the CU's 160)
     const size_t lds = resident_per_cu >= 8 ? 0 : (size_t)kCuLdsBytes / (size_t)(resident_per_cu + 1) + 1024;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = grad_bytes == 4 ? launch_layout<4>(l, a, lds, s) : launch_layout<2>(l, a, lds, s);

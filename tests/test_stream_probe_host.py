@@ -63,7 +63,7 @@ def test_probe_rejects_bad_arguments_before_any_device_call():
     assert call(storage=0) == -1 and call(storage=4) == -1
     assert call(grad_bytes=3) == -1
     assert call(n_blocks=0) == -1 and call(n_blocks=1 << 24) == -1
-    assert call(cap=0) == -1 and call(cap=9) == -1
+    assert call(cap=1) == -1 and call(cap=9) == -1
     assert call(param=None) == -1 and call(m=ctypes.c_void_p((1 << 20) + 8)) == -1
     assert call(scales=None) == -1          # 8-bit moments need their scales
     assert call(amsgrad=1) == -1            # ... and AMSGrad its maximum
