@@ -99,7 +99,7 @@ def _block_list(numels, block=2048):
 
 def host_threads():
     """Host cores the oracle may use: the process's CPU affinity, capped by
-    OMP_NUM_THREADS when set (the GPU machine allots a share of its cores)."""
+    OMP_NUM_THREADS when set (a shared host may allot a share of its cores)."""
     n = len(os.sched_getaffinity(0))
     cap = os.environ.get("OMP_NUM_THREADS")
     if cap and cap.isdigit() and int(cap) > 0:
@@ -336,7 +336,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the step needs no "
+        print("bench.py: the benchmark measures one GPU only (the step needs no "
               "exchange between GPUs); run with --gpus 1", file=sys.stderr, flush=True)
         sys.exit(2)
 

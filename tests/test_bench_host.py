@@ -15,7 +15,7 @@ import workloads  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():
-    # the step needs no exchange between GPUs and this build measures one:
+    # the step needs no exchange between GPUs and the benchmark measures one:
     # --gpus 2 exits with status 2 and a message, printing no bench line
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
