@@ -45,9 +45,11 @@
  * torch.optim.AdamW/Adam(amsgrad=True) in the fp32 mode, the running
  * maximum's draws against PyTorch's Philox engine, one 8-bit step from a
  * non-zero state composed from pinned parts.
- * Parity unpinned: the absolute values of a multi-step trajectory beyond what
- * the composition test of one step from a non-zero state pins (the pages
- * print no worked example).
+ * Multi-step trajectories: every step of 8-step runs checked from the state
+ * the oracle holds before it (decoded, one torch.optim.AdamW step, the
+ * result re-encoded by the pinned rules), in the bf16, 8-bit and fp32-m
+ * modes with nearest and stochastic rounding.  The pages print no worked
+ * multi-step example to compare a trajectory with as a whole.
  */
 #include <math.h>
 #include <stdint.h>

@@ -8,7 +8,9 @@ References used here, none of them the oracle's own code:
     and a textbook fp64 Adam, for the oracle's fp32-moment mode;
   * one 8-bit step from a non-zero state composed from pinned parts: the
     dequantized state fed to torch.optim.AdamW, then brute-force nearest
-    codes of the new moments;
+    codes of the new moments; the same check on every step of 8-step
+    trajectories (bf16, 8-bit and fp32-m modes, nearest and stochastic
+    rounding);
   * structural invariants (code ranges, exact block maxima, tensor-order
     permutation, per-tensor independence).
 """
@@ -218,6 +220,86 @@ def test_one_quantized_step_composes_pinned_parts(orc, storage):
             dist = np.abs(vals[None, :] - x.astype(np.float64)[:, None])
             chosen = dist[np.arange(x.size), codes - alphabet[0]]
             assert np.all(chosen <= dist.min(axis=1) + 4 * U * float(A))
+
+
+def _decoded_state(orc, st, n, blocks):
+    """The oracle's stored moments of a one-tensor state, decoded to fp32."""
+    if st.storage == "bf16":
+        return (orc.f32_from_bf16(st.m_bf16[:n]).astype(np.float32),
+                orc.f32_from_bf16(st.v_bf16[:n]).astype(np.float32))
+    m = np.empty(n, np.float32)
+    v = np.empty(n, np.float32)
+    for b, (s, e) in enumerate(blocks):
+        if st.storage == "q8":
+            m[s:e] = orc.dequantize_block(st.m_codes[s:e], True, float(st.m_scale[b]))
+        else:
+            m[s:e] = st.m_f32[s:e]
+        v[s:e] = orc.dequantize_block(st.v_codes[s:e], False, float(st.v_scale[b]))
+    return m, v
+
+
+@pytest.mark.parametrize("storage,stochastic", [("bf16", False), ("q8", False), ("q8", True),
+                                                ("q8_v_only", False), ("q8_v_only", True)])
+def test_every_step_of_a_trajectory_composes_pinned_parts(orc, storage, stochastic):
+    # Eight steps from a zero state; each one checked from the state the
+    # oracle actually holds before it: that state decoded, one
+    # torch.optim.AdamW step, and the stored result re-encoded by the pinned
+    # rules (bf16: PyTorch's cast; 8-bit: the block maximum as scale and the
+    # nearest code of the whole alphabet by brute force, or under stochastic
+    # rounding a code whose value lies within one step of the moment).  So
+    # every step of a multi-step trajectory is pinned, not only the first.
+    n = 2048 * 2 + 700
+    blocks = [(0, 2048), (2048, 4096), (4096, n)]
+    p0 = workloads.host_params(108, [n])[0]
+    st = _fresh(orc, [n], storage)
+    pp = [p0.copy()]
+    for t in range(1, 9):
+        g = workloads.host_grads(108, [n], t)[0]
+        m_old, v_old = _decoded_state(orc, st, n, blocks)
+        tp = torch.tensor(pp[0].copy(), requires_grad=True)
+        opt = torch.optim.AdamW([tp], lr=HP32["lr"], betas=(HP32["beta1"], HP32["beta2"]),
+                                eps=HP32["eps"], weight_decay=HP32["weight_decay"], foreach=False)
+        opt.state[tp] = {"step": torch.tensor(float(t - 1)),
+                         "exp_avg": torch.tensor(m_old), "exp_avg_sq": torch.tensor(v_old)}
+        tp.grad = torch.tensor(g)
+        opt.step()
+        p_before = pp[0].copy()
+        m_new, v_new = st.step(pp, [g], t=t, stochastic=stochastic, seed=9, want_moments=True, **HP)
+        m_new, v_new = m_new[:n], v_new[:n]
+        want_p = tp.detach().numpy().astype(np.float64)
+        # the two fp32 evaluations differ by a few roundings of |p| and of
+        # the update itself (which can exceed lr where a decoded v is 0 and
+        # the fp32 first moment is not)
+        upd = np.abs(want_p - p_before.astype(np.float64))
+        tol = _trajectory_tol(want_p, p_before, 1, HP["lr"]) + 8 * U * upd
+        assert np.all(np.abs(pp[0].astype(np.float64) - want_p) <= tol), t
+        tm = opt.state[tp]["exp_avg"].numpy()
+        tv = opt.state[tp]["exp_avg_sq"].numpy()
+        assert np.max(np.abs(m_new - tm)) <= 1e-6 * np.abs(tm).max(), t
+        assert np.max(np.abs(v_new - tv)) <= 1e-6 * np.abs(tv).max(), t
+        if storage == "bf16":
+            for x, h in ((m_new, st.m_bf16[:n]), (v_new, st.v_bf16[:n])):
+                want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                assert np.array_equal(h, want), t
+            continue
+        for b, (s, e) in enumerate(blocks):
+            checks = [(v_new[s:e], st.v_codes[s:e].astype(np.int64), st.v_scale[b], False)]
+            if storage == "q8":
+                checks.append((m_new[s:e], st.m_codes[s:e].astype(np.int64), st.m_scale[b], True))
+            else:
+                assert np.array_equal(st.m_f32[s:e], m_new[s:e]), t
+            for x, codes, A, signed in checks:
+                assert A == np.abs(x).max(), t
+                qmax = 127 if signed else 255
+                if stochastic:
+                    got = orc.dequantize_block(codes, signed, float(A)).astype(np.float64)
+                    assert np.all(np.abs(got - x.astype(np.float64)) <= float(A) / qmax * (1 + 8 * U)), t
+                    continue
+                alphabet = np.arange(-qmax if signed else 0, qmax + 1)
+                vals = orc.dequantize_block(alphabet, signed, float(A)).astype(np.float64)
+                dist = np.abs(vals[None, :] - x.astype(np.float64)[:, None])
+                chosen = dist[np.arange(x.size), codes - alphabet[0]]
+                assert np.all(chosen <= dist.min(axis=1) + 4 * U * float(A)), t
 
 
 @pytest.mark.parametrize("stochastic", [False, True])

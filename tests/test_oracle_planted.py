@@ -15,6 +15,8 @@ Mistakes planted (one per build):
   no_omb1       first-moment EMA without the (1 - beta1) factor
   bf16_ties_up  bf16 packing rounds exact halves up instead of to even
   weyl_key      Philox key bumped with the wrong Weyl constant
+  v_signed      the 8-bit step decodes its stored v codes in the signed
+                alphabet (step 1 is right, every later step is not)
 """
 import os
 import shutil
@@ -44,6 +46,8 @@ MUTATIONS = [
     ("no_omb1", "fmaf(h->beta1, m_old, omb1 * g)", "fmaf(h->beta1, m_old, g)"),
     ("bf16_ties_up", "(dropped == 0x8000u && (upper & 1u))", "(dropped == 0x8000u)"),
     ("weyl_key", "k[0] += 0x9E3779B9u;", "k[0] += 0x9E3779B7u;"),
+    ("v_signed", "m_old = orc_dequantize(q->mq[j], q->ms[0], 1);\n            v_old = orc_dequantize(q->vq[j], q->vs[0], 0);",
+     "m_old = orc_dequantize(q->mq[j], q->ms[0], 1);\n            v_old = orc_dequantize(q->vq[j], q->vs[0], 1);"),
 ]
 
 
