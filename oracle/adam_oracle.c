@@ -43,8 +43,8 @@
  * first step equal to the dynamic one, scales unchanged once set, later codes
  * nearest in the codebook of the kept scale (brute force).  AMSGrad:
  * torch.optim.AdamW/Adam(amsgrad=True) in the fp32 mode, the running
- * maximum's draws against PyTorch's Philox engine, one 8-bit step from a
- * non-zero state composed from pinned parts.
+ * maximum's draws against PyTorch's Philox engine, every 8-bit step of a
+ * 6-step run composed from pinned parts.
  * Multi-step trajectories: every step of 8-step runs checked from the state
  * the oracle holds before it (decoded, one torch.optim.AdamW step, the
  * result re-encoded by the pinned rules), in the bf16, 8-bit and fp32-m

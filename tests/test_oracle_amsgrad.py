@@ -7,9 +7,10 @@ References used here, none of them the oracle's own code:
   * the first step from a zero state: the maximum equals v, so AMSGrad
     reproduces the plain step (pinned in test_oracle_adam.py) bit for bit;
   * PyTorch's header-only Philox engine for the maximum's own draws;
-  * one 8-bit step from a non-zero state composed from pinned parts: the
+  * every 8-bit step of a 6-step run composed from pinned parts: the
     dequantized state (m, v and the maximum) fed to torch AdamW with
-    amsgrad, then brute-force nearest codes of the new maximum.
+    amsgrad, then brute-force nearest codes of the new maximum (or, under
+    stochastic rounding, the codes its pinned draws give).
 """
 import os
 import subprocess
@@ -124,56 +125,62 @@ def test_maximum_draws_use_the_second_counter_stream(orc, philox_ref):
 
 @pytest.mark.parametrize("storage", ["q8", "q8_v_only"])
 @pytest.mark.parametrize("stochastic", [False, True])
-def test_one_quantized_step_composes_pinned_parts(orc, storage, stochastic):
+def test_every_quantized_step_composes_pinned_parts(orc, storage, stochastic):
+    # every step of a 6-step run, each from the state the oracle holds
+    # before it: decoded, one torch AdamW(amsgrad=True) step, the running
+    # maximum re-encoded by the pinned rules
     n = 2048 * 2 + 700
     p = workloads.host_params(303, [n])[0]
     gs = _shrinking_grads(303, n, 6)
     st = orc.OracleState([n], storage, amsgrad=True)
     pp = [p.copy()]
-    for t in range(1, 6):
-        st.step(pp, [gs[t - 1]], t=t, stochastic=stochastic, seed=9, **HP)
-    t = 6
-    g = gs[t - 1]
     blocks = [(0, 2048), (2048, 4096), (4096, n)]
-    deq = {k: np.empty(n, np.float32) for k in ("m", "v", "w")}
-    for b, (s, e) in enumerate(blocks):
-        if storage == "q8":
-            deq["m"][s:e] = orc.dequantize_block(st.m_codes[s:e], True, float(st.m_scale[b]))
-        else:
-            deq["m"][s:e] = st.m_f32[s:e]
-        deq["v"][s:e] = orc.dequantize_block(st.v_codes[s:e], False, float(st.v_scale[b]))
-        deq["w"][s:e] = orc.dequantize_block(st.vmax_codes[s:e], False,
-                                             float(st.vmax_scale[b]))
-    tp = torch.tensor(pp[0].copy(), requires_grad=True)
-    opt = torch.optim.AdamW([tp], lr=HP32["lr"], betas=(HP32["beta1"], HP32["beta2"]),
-                            eps=HP32["eps"], weight_decay=HP32["weight_decay"], amsgrad=True,
-                            foreach=False)
-    opt.state[tp] = {"step": torch.tensor(float(t - 1)), "exp_avg": torch.tensor(deq["m"]),
-                     "exp_avg_sq": torch.tensor(deq["v"]),
-                     "max_exp_avg_sq": torch.tensor(deq["w"])}
-    tp.grad = torch.tensor(g)
-    opt.step()
-    m_new, v_new, w_new = (a[:n] for a in st.step(pp, [g], t=t, stochastic=stochastic, seed=9,
-                                                    want_moments=True, **HP))
-    want = tp.detach().numpy()
-    assert np.all(np.abs(pp[0].astype(np.float64) - want) <= _tol(want, pp[0], 1, HP["lr"]))
-    tw = opt.state[tp]["max_exp_avg_sq"].numpy()
-    assert np.max(np.abs(w_new - tw)) <= 1e-6 * np.abs(tw).max()
-    assert np.all(w_new >= v_new) and np.mean(w_new > v_new) > 0.5
     alphabet = np.arange(0, 256)
-    for b, (s, e) in enumerate(blocks):
-        A = st.vmax_scale[b]
-        assert A == w_new[s:e].max()
-        codes = st.vmax_codes[s:e].astype(np.int64)
-        vals = orc.dequantize_block(alphabet, False, float(A)).astype(np.float64)
-        dist = np.abs(vals[None, :] - w_new[s:e].astype(np.float64)[:, None])
-        if stochastic:
-            # one of the two codes around the value
-            lo = np.floor(w_new[s:e].astype(np.float64) * 255 / float(A))
-            assert np.all((codes >= lo - 1) & (codes <= lo + 2))
-            draws = orc.sr_draws(9, t, s, e - s, 2)
-            want_codes, _ = orc.quantize_with_stat(w_new[s:e], False, float(A), draws)
-            assert np.array_equal(codes, want_codes)
-        else:
-            chosen = dist[np.arange(e - s), codes]
-            assert np.all(chosen <= dist.min(axis=1) + 4 * U * float(A))
+    for t in range(1, 7):
+        g = gs[t - 1]
+        deq = {k: np.empty(n, np.float32) for k in ("m", "v", "w")}
+        for b, (s, e) in enumerate(blocks):
+            if storage == "q8":
+                deq["m"][s:e] = orc.dequantize_block(st.m_codes[s:e], True, float(st.m_scale[b]))
+            else:
+                deq["m"][s:e] = st.m_f32[s:e]
+            deq["v"][s:e] = orc.dequantize_block(st.v_codes[s:e], False, float(st.v_scale[b]))
+            deq["w"][s:e] = orc.dequantize_block(st.vmax_codes[s:e], False,
+                                                 float(st.vmax_scale[b]))
+        tp = torch.tensor(pp[0].copy(), requires_grad=True)
+        opt = torch.optim.AdamW([tp], lr=HP32["lr"], betas=(HP32["beta1"], HP32["beta2"]),
+                                eps=HP32["eps"], weight_decay=HP32["weight_decay"], amsgrad=True,
+                                foreach=False)
+        opt.state[tp] = {"step": torch.tensor(float(t - 1)), "exp_avg": torch.tensor(deq["m"]),
+                         "exp_avg_sq": torch.tensor(deq["v"]),
+                         "max_exp_avg_sq": torch.tensor(deq["w"])}
+        tp.grad = torch.tensor(g)
+        opt.step()
+        p_before = pp[0].copy()
+        m_new, v_new, w_new = (a[:n] for a in st.step(pp, [g], t=t, stochastic=stochastic, seed=9,
+                                                        want_moments=True, **HP))
+        want = tp.detach().numpy().astype(np.float64)
+        # a few roundings of |p| and of the update itself
+        tol = _tol(want, p_before, 1, HP["lr"]) + 8 * U * np.abs(want - p_before.astype(np.float64))
+        assert np.all(np.abs(pp[0].astype(np.float64) - want) <= tol), t
+        tw = opt.state[tp]["max_exp_avg_sq"].numpy()
+        assert np.max(np.abs(w_new - tw)) <= 1e-6 * np.abs(tw).max(), t
+        assert np.all(w_new >= v_new), t
+        for b, (s, e) in enumerate(blocks):
+            A = st.vmax_scale[b]
+            assert A == w_new[s:e].max(), t
+            codes = st.vmax_codes[s:e].astype(np.int64)
+            vals = orc.dequantize_block(alphabet, False, float(A)).astype(np.float64)
+            dist = np.abs(vals[None, :] - w_new[s:e].astype(np.float64)[:, None])
+            if stochastic:
+                # one of the two codes around the value, from the maximum's draws
+                lo = np.floor(w_new[s:e].astype(np.float64) * 255 / float(A))
+                assert np.all((codes >= lo - 1) & (codes <= lo + 2)), t
+                draws = orc.sr_draws(9, t, s, e - s, 2)
+                want_codes, _ = orc.quantize_with_stat(w_new[s:e], False, float(A), draws)
+                assert np.array_equal(codes, want_codes), t
+            else:
+                chosen = dist[np.arange(e - s), codes]
+                assert np.all(chosen <= dist.min(axis=1) + 4 * U * float(A)), t
+    # the shrinking gradients leave the maximum above v for most elements
+    assert np.mean(w_new > v_new) > 0.5
