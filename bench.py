@@ -171,10 +171,12 @@ def apply_overrides(cfg, args):
         if cfg.storage == "bf16":
             sys.exit("bench.py: --static-scales applies to 8-bit storage only")
         hp["static_scales"] = True
-    if args.nearest:
+    if args.nearest and args.stochastic:
+        sys.exit("bench.py: --nearest and --stochastic exclude each other")
+    if args.nearest or args.stochastic:
         if cfg.storage == "bf16":
-            sys.exit("bench.py: --nearest applies to 8-bit storage only")
-        hp["stochastic"] = False
+            sys.exit("bench.py: --nearest / --stochastic apply to 8-bit storage only")
+        hp["stochastic"] = bool(args.stochastic)
     if args.percentile is not None:
         if cfg.storage == "bf16":
             sys.exit("bench.py: --percentile applies to 8-bit storage only")
@@ -343,6 +345,8 @@ def main():
                     help="8-bit sets: percentile block statistic (e.g. 99.9) instead of the set's own")
     ap.add_argument("--nearest", action="store_true",
                     help="8-bit sets: nearest-even rounding instead of the set's stochastic rounding")
+    ap.add_argument("--stochastic", action="store_true",
+                    help="8-bit sets: Philox stochastic rounding instead of the set's nearest rounding")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's device copy of 4 GiB (counter calibration run)")
     ap.add_argument("--stream-probe", action="store_true",
@@ -389,7 +393,8 @@ def main():
     # percentile, nearest-rounding or AMSGrad run of a set has its own record
     # when one was taken; static scales have none)
     key = None if args.static_scales else cfg.name + ("_amsgrad" if cfg.amsgrad else "") + (
-        "_nearest" if args.nearest else "") + ("" if args.percentile is None else f"_percentile{args.percentile}")
+        "_nearest" if args.nearest else "") + ("_stochastic" if args.stochastic else "") + (
+        "" if args.percentile is None else f"_percentile{args.percentile}")
     rec = time_workload(cfg, hp, args.steps, args.warmup, args.grad_buffers, key)
     out = {
         "metric": "Adam step Gparams/s + achieved HBM GB/s (% of 8 TB/s), 8-bit and bf16 moments",

@@ -1336,10 +1336,13 @@ adam_step_kernel(StepArgs a) {
 // shaped set with bf16 gradients +7% over uncapped, ViT-Base with fp32
 // gradients unchanged); fp32 m + 8-bit v with the percentile walk and
 // nearest rounding (one walk per block) at most 4 (Llama-7B shaped set
-// +2.6%).  Stochastic rounding, the radix select and the walks over two or
-// three moments spend longer per block and need every resident workgroup to
-// keep enough bytes in flight (a cap of 4 cost them 5-9%), so they are not
-// capped.
+// +2.6%).  Stochastic rounding with the block maximum and bf16 gradients
+// (no AMSGrad) at most 5 (GPT-1.3B shaped set, three boxes: +0.4%, +0.8%,
+// +2.4%; 4 per CU -6%; with fp32 gradients 5 per CU cost 1.7%, with AMSGrad
+// 1.1%).  The other stochastic-rounding variants, the radix select and the
+// walks over two or three moments spend longer per block and need every
+// resident workgroup to keep enough bytes in flight (a cap of 4 cost them
+// 5-9%), so they are not capped.
 constexpr int kCuLdsBytes = 160 * 1024;
 #ifndef ADAM_BF16_RESIDENT_PER_CU
 #define ADAM_BF16_RESIDENT_PER_CU 3
@@ -1350,6 +1353,9 @@ constexpr int kCuLdsBytes = 160 * 1024;
 #ifndef ADAM_Q8_RESIDENT_PER_CU
 #define ADAM_Q8_RESIDENT_PER_CU 8
 #endif
+#ifndef ADAM_Q8_SR_BF16G_RESIDENT_PER_CU
+#define ADAM_Q8_SR_BF16G_RESIDENT_PER_CU 5
+#endif
 constexpr size_t reserve_lds(int resident) { return resident >= 8 ? 0 : kCuLdsBytes / (resident + 1) + 1024; }
 constexpr uint32_t kMaxGrid = (1u << 24) - 1;  // grid.x * 256 work-items < 2^32
 
@@ -1358,8 +1364,10 @@ hipError_t launch_one(const StepArgs &a, hipStream_t stream) {
     const uint32_t grid = std::min<uint32_t>(a.n_all, kMaxGrid);
     if (grid == 0) return hipSuccess;
     constexpr bool kLight = !kSR && (kPct == kPctNone || (kPct == kPctTop && kStore == kStoreQ8VOnly && !kAms));
+    constexpr bool kSrBf16g = kSR && kGradBf16 && !kAms && kPct == kPctNone;
     constexpr int kResident = kStore == kStoreBf16 ? ADAM_BF16_RESIDENT_PER_CU
                               : kLight             ? ADAM_Q8_NEAREST_RESIDENT_PER_CU
+                              : kSrBf16g           ? ADAM_Q8_SR_BF16G_RESIDENT_PER_CU
                                                    : ADAM_Q8_RESIDENT_PER_CU;
     constexpr size_t kStaticLds = sizeof(BlockLds) + sizeof(SelectLds<kPct, kAms ? 3 : 2>);
     constexpr size_t kDyn = reserve_lds(kResident) > kStaticLds ? reserve_lds(kResident) - kStaticLds : 0;
