@@ -155,14 +155,15 @@ _CHECKED_SETS = 8  # tensor sets remembered per state (callers rotate gradient b
 
 
 def _checked_pointers(state, params, grads):
-    """Device pointers of params and grads.  The full tensor checks run when
-    the (params, grads) tensor objects and their data pointers are not among
-    the last few sets checked on this state: a caller stepping the same
-    tensors, or rotating a few gradient buffers, pays two passes of
-    data_ptr() and an identity compare (~0.25 us per tensor) instead of the
-    checks (~1.5 us per tensor, which for a 150-tensor model outlast a step
-    of the kernel and would leave the GPU waiting on the host).  The state
-    holds the remembered tensors until they are pushed out or destroy()."""
+    """Device pointer arrays (ctypes) of params and grads.  The full tensor
+    checks run when the (params, grads) tensor objects and their data
+    pointers are not among the last few sets checked on this state: a caller
+    stepping the same tensors, or rotating a few gradient buffers, pays two
+    passes of data_ptr() and an identity compare (~0.25 us per tensor)
+    instead of the checks (~1.5 us per tensor, which for a 150-tensor model
+    outlast a step of the kernel and would leave the GPU waiting on the
+    host), and reuses the set's pointer arrays.  The state holds the
+    remembered tensors until they are pushed out or destroy()."""
     import torch
     ptr = torch.Tensor.data_ptr
     try:
@@ -175,11 +176,14 @@ def _checked_pointers(state, params, grads):
     for c in sets:
         if (c[2] == pp and c[3] == gp and len(c[0]) == len(params) and len(c[1]) == len(grads)
                 and all(map(operator.is_, c[0], params)) and all(map(operator.is_, c[1], grads))):
-            return pp, gp
+            return c[4], c[5]
     _check_step_tensors(state, params, grads)
-    sets.insert(0, (tuple(params), tuple(grads), pp, gp))
+    n = max(len(state.numels), 1)
+    P = (ctypes.c_void_p * n)(*pp)
+    G = (ctypes.c_void_p * n)(*gp)
+    sets.insert(0, (tuple(params), tuple(grads), pp, gp, P, G))
     del sets[_CHECKED_SETS:]
-    return pp, gp
+    return P, G
 
 
 def _stream(stream):
@@ -255,10 +259,7 @@ def adam_step(state, params, grads, *, lr, beta1, beta2, eps, weight_decay, t,
     absmax block statistic; static_scales keeps each block's scale once set.
     expect: (storage, grad_dtype[, block_size[, options]]) the caller believes
     the state has (default: the state's own layout)."""
-    n = len(state.numels)
-    pp, gp = _checked_pointers(state, params, grads)
-    P = (ctypes.c_void_p * max(n, 1))(*pp)
-    G = (ctypes.c_void_p * max(n, 1))(*gp)
+    P, G = _checked_pointers(state, params, grads)
     hp = _hparams(lr, beta1, beta2, eps, weight_decay, t, decoupled, stochastic, percentile, seed,
                   static_scales)
     lay = state.layout if expect is None else _layout(*expect)

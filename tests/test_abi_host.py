@@ -338,7 +338,14 @@ def test_step_checks_rerun_when_tensors_change(monkeypatch):
     B._checked_pointers(st, ps, gs2)
     assert len(full) == 2
     ps[1].set_(torch.zeros(7).untyped_storage())  # same object, new data pointer
-    B._checked_pointers(st, ps, gs2)
+    P, G = B._checked_pointers(st, ps, gs2)
+    assert len(full) == 3
+    # the pointer arrays handed to the C call are the current ones, also when
+    # they come from the remembered set
+    for _ in range(2):
+        assert [P[k] for k in range(2)] == [t.data_ptr() for t in ps]
+        assert [G[k] for k in range(2)] == [t.data_ptr() for t in gs2]
+        P, G = B._checked_pointers(st, ps, gs2)
     assert len(full) == 3
     # rotating a few gradient sets stays on the fast path
     sets = [[torch.zeros(100), torch.zeros(7)] for _ in range(4)]
