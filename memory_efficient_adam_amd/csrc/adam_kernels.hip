@@ -1339,7 +1339,7 @@ adam_step_kernel(StepArgs a) {
 // +2.6%).  Stochastic rounding with the block maximum and bf16 gradients
 // (no AMSGrad) at most 5 (GPT-1.3B shaped set, three boxes: +0.4%, +0.8%,
 // +2.4%; 4 per CU -6%; with fp32 gradients 5 per CU cost 1.7%, with AMSGrad
-// 1.1%).  The other stochastic-rounding variants, the radix select and the
+// 1.1%; the fp32-m storage takes the same cap, not measured there).  The other stochastic-rounding variants, the radix select and the
 // walks over two or three moments spend longer per block and need every
 // resident workgroup to keep enough bytes in flight (a cap of 4 cost them
 // 5-9%), so they are not capped.
