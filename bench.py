@@ -17,9 +17,11 @@ Each record: Gparams/s, the roofline of the step kernel (algorithmic bytes
 per launch / average launch time from HIP events on the launch stream,
 against the 8 TB/s HBM peak; HBM traffic from rocprofv3 FETCH_SIZE /
 WRITE_SIZE counters when a committed counter summary matches the current
-kernel source) and the CPU oracle timed on the same workload recipe, once on
-one thread and once on all the host cores it may use (threads over disjoint
-block ranges of the oracle's sampled-block entry point).
+kernel source; the stream probe's rate for the same blocks on this box, the
+access pattern's ceiling) and the CPU oracle timed on the same workload
+recipe, once on one thread and once on all the host cores it may use
+(threads over disjoint block ranges of the oracle's sampled-block entry
+point).
 """
 import argparse
 import dataclasses
@@ -313,6 +315,23 @@ def time_stream_probe(cfg, steps, warmup, caps=PROBE_CAPS):
             "resident_per_cu": rates, "best_cap": int(best), "best": rates[best]}
 
 
+def pattern_ceiling(cfg, roofline, steps=20, warmup=5):
+    """The stream probe on the workload's blocks on this box (best residency
+    cap), and the step's fraction of it: the same bytes in the same pattern
+    without the arithmetic, which is what the access pattern itself reaches
+    here.  None if the probe library is missing or the probe fails (the
+    step's own record stands without it)."""
+    try:
+        probe = time_stream_probe(cfg, steps, warmup)
+    except Exception as e:  # a measurement aid: never let it cost the bench line
+        print(f"bench.py: stream probe skipped ({type(e).__name__}: {e})", file=sys.stderr, flush=True)
+        return None
+    best = probe["best"]
+    return {"best_cap": probe["best_cap"], "frac": best["frac"], "GB/s": best["GB/s"],
+            "step_over_ceiling": round(roofline["frac"] / best["frac"], 4),
+            "source": "bench.py stream probe: the step's loads and stores without its arithmetic"}
+
+
 # the 8-bit workloads timed beside the headline (bf16-moment) workload, with
 # the host-oracle sample size for each (blocks) and the grad buffers rotated
 MODES = [("vit_q8", 4096, 4), ("gpt1p3b_q8_sr", 4096, 4), ("llama7b_mf32_vq8_pct", 4096, 2)]
@@ -347,6 +366,8 @@ def main():
                     help="8-bit sets: nearest-even rounding instead of the set's stochastic rounding")
     ap.add_argument("--stochastic", action="store_true",
                     help="8-bit sets: Philox stochastic rounding instead of the set's nearest rounding")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the stream-probe ceiling of each record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time torch's device copy of 4 GiB (counter calibration run)")
     ap.add_argument("--stream-probe", action="store_true",
@@ -424,6 +445,10 @@ def main():
             m["meets_target"] = m["roofline"]["frac"] >= TARGET_FRAC
             modes.append((m, mcfg, sample_blocks))
         out["modes"] = [m for m, _, _ in modes]
+    if not args.no_ceiling:
+        out["roofline"]["pattern_ceiling"] = pattern_ceiling(cfg, out["roofline"])
+        for m, mcfg, _ in modes:
+            m["roofline"]["pattern_ceiling"] = pattern_ceiling(mcfg, m["roofline"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, hp)
         for m, mcfg, sample_blocks in modes:

@@ -1,7 +1,7 @@
 """bench.py end to end on the GPU, on the smallest workload (one 1M-parameter
 tensor, 8-bit moments): the JSON line carries the fields the benchmark
-reports, with values consistent with each other, and the stream-probe mode
-reports every residency cap."""
+reports (with the stream probe's ceiling), with values consistent with each
+other, and the stream-probe mode reports every residency cap."""
 import json
 import os
 import subprocess
@@ -36,6 +36,10 @@ def test_bench_line_on_a_small_workload():
     assert abs(d["value"] - cfg["params"] / sec / 1e9) <= 1e-3 * d["value"] + 1e-3
     assert abs(roof["achieved"] - roof["algorithmic_bytes_per_launch"] / sec / 1e9) <= 0.1 + 1e-3 * roof["achieved"]
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    # the stream probe's ceiling on the same blocks, and the step's fraction of it
+    ceil = roof["pattern_ceiling"]
+    assert ceil["best_cap"] in (2, 3, 4, 5, 6, 8) and 0 < ceil["frac"] < 1.5
+    assert abs(ceil["step_over_ceiling"] - roof["frac"] / ceil["frac"]) < 1e-3
 
 
 def test_stream_probe_mode_on_a_small_workload():
