@@ -78,6 +78,7 @@ MODES = [
     ("q8_v_only", "bf16", False, 99.9, True),
     ("q8_v_only", "bf16", True, 99.9, True),
     ("q8_v_only", "f32", True, None, False),
+    ("q8_v_only", "bf16", True, None, True),
 ]
 
 
