@@ -529,9 +529,11 @@ __device__ void block_select_n(const float *const (&x)[N], const bool (&act)[N],
 // walk_covers).  With two or three moments (8-bit m and v, or AMSGrad) each
 // lane writes its top-4 keys of each moment to LDS and, after one barrier,
 // wave k walks moment k's 1024 keys alone (lane_top4 / top_select below):
-// one walk per moment instead of one per wave and moment (ViT-Base 8-bit at
-// 99.9 +2.7%, GPT-1.3B SR +3.4%, with AMSGrad +3.6%).  With v alone (fp32
-// m) the four waves walk their own keys, which measured 0.7% faster there:
+// one walk per moment instead of one per wave and moment plus a merge (one
+// box, interleaved 100-step runs: ViT-Base 8-bit at 99.9 +4.3%, GPT-1.3B SR
+// +5.4%, with AMSGrad +6.2%).  With v alone (fp32 m) the four waves walk
+// their own keys; the lane lists gained nothing there (-1.4%, within the
+// run-to-run spread of that set):
 //   wave_top:  each wave takes its own keys' largest value, counts it,
 //              drops it, and repeats until at least `need` keys are counted;
 //              the (value, count) list goes to LDS.  No barrier.
