@@ -610,7 +610,9 @@ __device__ __forceinline__ void wave_top(const float (&x)[kItems], uint32_t need
 // The walks serve need <= 4 (percentiles of 99.85 and above for a full
 // block, the pages' default 99.9 among them); from need 5 on, the radix
 // select is faster (8-bit ViT-Base set, percentile 99.5 (need 12): 317
-// against 288 Gparams/s for walks over per-lane top-4 lists).
+// against 288 Gparams/s for per-wave walks over per-lane top-4 lists, 342
+// against 322 for one selecting wave per moment over the union of the lane
+// lists, whose serial rounds grow with need: 338 against 285 at 99.0).
 constexpr uint32_t kWalkNeed = 4;
 
 __device__ __forceinline__ bool wave_top_lanes(const float (&x)[kItems], uint32_t need, uint32_t *val,
