@@ -4,7 +4,8 @@
 // reads the block's params, grads, stored moments and old scales once,
 // keeps the updated moments in registers, reduces the block statistic
 // (DPP cross-lane steps + one cross-wave LDS step; for the percentile
-// statistic, per-wave walks down the top values or an LDS radix select;
+// statistic, walks down the top values (of the lanes' top-4 lists, or of
+// per-wave lists when v is the only 8-bit moment) or an LDS radix select;
 // skipped for a moment whose static scale is already set), requantizes and
 // writes params, moments and the new scales once.  With AMSGrad the running
 // maximum of v travels the same way as v.  The step is a streaming map over
