@@ -175,9 +175,11 @@ def test_static_scales_radix_select_with_one_moment_kept(ams, pct):
 
 # percentiles whose full-block rank lands near the top: need = 2048 - rank
 # keys at or above the statistic, with rank = floor(p/100 * 2047).  Up to
-# 16 the kernel walks down the top values per wave, beyond it it takes the
-# radix select; 2032.5 and 2031.5 sit on either side of that switch.
-NEAR_TOP = [100.0, 99.9, 99.5, 100.0 * 2032.5 / 2047, 100.0 * 2031.5 / 2047]
+# need 4 the kernel walks down the top values, beyond it it takes the radix
+# select; 2044.5 (need 4) and 2043.5 (need 5) sit on either side of that
+# switch, 2032.5 and 2031.5 (need 16, 17) further into the radix select.
+NEAR_TOP = [100.0, 99.9, 100.0 * 2044.5 / 2047, 100.0 * 2043.5 / 2047, 99.5,
+            100.0 * 2032.5 / 2047, 100.0 * 2031.5 / 2047]
 
 
 @pytest.mark.parametrize("pct", NEAR_TOP)
