@@ -1410,10 +1410,12 @@ adam_step_kernel(StepArgs a) {
         // XCD takes runs of 16 consecutive blocks, the runs dealt round-robin
         // (a bijection on the first n - n mod 128 blocks; the rest keep their
         // order).  Measured +2% for the 8-bit nearest-rounding step and ~+1%
-        // for the percentile one; the stochastic-rounding steps keep plain
-        // order (the GPT-1.3B shaped set: -1.2% with it).
+        // for the percentile one; with stochastic rounding +2.9% on the
+        // ViT-Base 8-bit set (fp32 grads), +1.1% on the fp32-m + 8-bit-v
+        // shard set, level on the GPT-1.3B set.  Stochastic rounding with
+        // AMSGrad keeps plain order (GPT-1.3B shaped set: -3.1% with it).
         uint32_t i = i0;
-        if (!kSR && gridDim.x == a.n_all && i0 < a.n_all - a.n_all % 128u) {
+        if (!(kSR && kAms) && gridDim.x == a.n_all && i0 < a.n_all - a.n_all % 128u) {
             const uint32_t x = i0 & 7u, k = i0 >> 3;
             i = ((k >> 4) << 7) + (x << 4) + (k & 15u);
         }
