@@ -754,16 +754,20 @@ def test_full_size_sampled_blocks_static_scales():
 @pytest.mark.parametrize("name", ["vit_bf16", "vit_q8", "gpt1p3b_q8_sr",
                                   "llama7b_mf32_vq8_pct", "llama7b_shard8_mf32_vq8_pct",
                                   "vit_q8@99.0", "vit_q8@50.0", "vit_q8@99.9",
-                                  "gpt1p3b_q8_sr@99.9"])
+                                  "gpt1p3b_q8_sr@99.9", "vit_q8+sr", "vit_q8+sr@99.9"])
 def test_full_size_sampled_blocks(name):
     # name@p: the same set with the percentile-p block statistic (the top
-    # walks serve 99.85 and above, the radix select the rest), in the
-    # benchmark's launch configuration
+    # walks serve 99.85 and above, the radix select the rest); name+sr: with
+    # stochastic rounding (fp32 grads); in the benchmark's launch
+    # configuration (XCD block order included)
     base, _, pct = name.partition("@")
+    base, _, sr = base.partition("+")
     cfg = workloads.CONFIGS[base]
+    if sr:
+        cfg = dataclasses.replace(cfg, hp=dict(cfg.hp, stochastic=True), name=f"{base}_sr")
     if pct:
         cfg = dataclasses.replace(cfg, hp=dict(cfg.hp, percentile=float(pct)),
-                                  name=f"{base}_percentile{pct}")
+                                  name=f"{cfg.name}_percentile{pct}")
     log(f"full-size {name}: {sum(cfg.numels())} params, {cfg.steps} steps")
     stats = run_sampled_parity(cfg, log=log)
     # every step compared at least the sampled blocks' params (and codes)
